@@ -1,0 +1,188 @@
+"""FP64 CPU oracle for causal prefill attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` import this module.  The library,
+its C ABI and its Python binding never import, call or link it, and it
+imports nothing from them.
+
+What is computed (the plain definition, written out):
+
+For each packed sequence ``s`` (tokens ``cu[s] .. cu[s+1]-1``, local indices
+``i, j`` in ``[0, L_s)``), each query head ``h`` and its key/value head
+``g = h // (n_q_heads / n_kv_heads)``:
+
+1. Inputs are converted exactly as passed to float64 (bf16, fp16 and fp32
+   all embed exactly).
+2. ``S = scale * Q[s, h] @ K[s, g]^T``, an ``L x L`` float64 matrix.
+3. Key ``j`` is visible to query ``i`` iff ``j <= i`` and (``W == 0`` or
+   ``j >= i - W + 1``): the causal bound ``kv_end = min(q_pos + 1,
+   seq_len)`` of the fused MLA prefill kernel on the atlas PR #69 page
+   (its re-audit commits), with the sliding window passed as a width where
+   0 means "off" (the cache-skip MLA fix commit on the same page, which
+   forwards ``sliding_window.unwrap_or(0)``).  ``W > 0`` keeps the W most
+   recent keys including the query's own position -- the "exact recent
+   ring" of the m40-llm AGENTS.md page ("Current Progress").
+4. ``P = rowsoftmax(S + mask)``: the row maximum over visible keys is
+   subtracted, the row is exponentiated and divided by its sum.  Every row
+   has at least one visible key (``j = i``).
+5. ``O[s, h] = P @ V[s, g]``.
+6. Sequences never see each other.
+
+The online-softmax recurrence that the GPU kernel uses (the fused MLA prefill
+commit on the atlas PR #69 page) is a reordering of steps 4-5 and is not
+used here.  The head grouping ``g = h // group`` is the consecutive GQA
+mapping (the m40-llm page's Qwen-shaped 16 Q / 2 KV packed-prefill test
+leaves the mapping unstated; this is the plain reading).
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "visibility",
+    "softmax_probs",
+    "attention_head",
+    "attention_varlen",
+    "attention_rows",
+    "visible_pairs",
+]
+
+
+def _as_f64(x) -> np.ndarray:
+    """Exact widening to float64 (torch tensors or numpy arrays)."""
+    if hasattr(x, "detach"):  # torch tensor: widen in torch, bf16 has no numpy dtype
+        import torch
+
+        return x.detach().to(device="cpu", dtype=torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _as_offsets(cu_seqlens) -> List[int]:
+    if hasattr(cu_seqlens, "detach"):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    return [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+
+
+def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """Key/value head read by query head ``h`` (consecutive grouping)."""
+    group = n_q_heads // n_kv_heads
+    return h // group
+
+
+def visibility(n_rows: int, n_cols: int, window: int) -> np.ndarray:
+    """Boolean ``[n_rows, n_cols]``: may query ``i`` attend to key ``j``."""
+    i = np.arange(n_rows)[:, None]
+    j = np.arange(n_cols)[None, :]
+    vis = j <= i
+    if window > 0:
+        vis &= j >= i - window + 1
+    return vis
+
+
+def softmax_probs(q_h, k_g, scale: float, window: int) -> np.ndarray:
+    """Attention probabilities ``P`` for one sequence and one head.
+
+    ``q_h``: ``[L, d]``, ``k_g``: ``[L, d]``.  Returns float64 ``[L, L]`` whose
+    rows sum to one over the visible keys and are exactly 0 elsewhere.
+    """
+    q_h = _as_f64(q_h)
+    k_g = _as_f64(k_g)
+    n = q_h.shape[0]
+    s = float(scale) * (q_h @ k_g.T)
+    vis = visibility(n, n, window)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def attention_head(q_h, k_g, v_g, scale: float, window: int) -> np.ndarray:
+    """``O = softmax(scale * Q K^T + mask) V`` for one sequence, one head."""
+    if np.shape(q_h)[0] == 0:
+        return np.zeros((0, np.shape(v_g)[1]), dtype=np.float64)
+    p = softmax_probs(q_h, k_g, scale, window)
+    return p @ _as_f64(v_g)
+
+
+def attention_varlen(q, k, v, cu_seqlens, n_q_heads: int, n_kv_heads: int,
+                     scale: float, window: int,
+                     workers: Optional[int] = None) -> np.ndarray:
+    """Packed varlen causal attention, float64 ``[T, n_q_heads, d_v]``.
+
+    ``q``: ``[T, n_q_heads, d]``; ``k``, ``v``: ``[T, n_kv_heads, d]``;
+    ``cu_seqlens``: ``n_seqs + 1`` offsets.  (sequence, head) pairs are
+    independent and run on a thread pool of ``workers`` threads (default:
+    all host cores), each with a single BLAS thread.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    cu = _as_offsets(cu_seqlens)
+    if n_q_heads % n_kv_heads != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    out = np.zeros((q.shape[0], n_q_heads, v.shape[2]), dtype=np.float64)
+    jobs = [(s, h) for s in range(len(cu) - 1) for h in range(n_q_heads)
+            if cu[s + 1] > cu[s]]
+
+    def run(job):
+        s, h = job
+        a, b = cu[s], cu[s + 1]
+        g = kv_head_of(h, n_q_heads, n_kv_heads)
+        out[a:b, h, :] = attention_head(q[a:b, h, :], k[a:b, g, :],
+                                        v[a:b, g, :], scale, window)
+
+    n_workers = workers if workers is not None else (os.cpu_count() or 1)
+    if n_workers <= 1 or len(jobs) <= 1:
+        for job in jobs:
+            run(job)
+        return out
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        with concurrent.futures.ThreadPoolExecutor(n_workers) as pool:
+            for f in [pool.submit(run, job) for job in jobs]:
+                f.result()
+    return out
+
+
+def attention_rows(q, k, v, cu_seqlens, n_q_heads: int, n_kv_heads: int,
+                   scale: float, window: int,
+                   rows: Iterable[Tuple[int, int]]) -> np.ndarray:
+    """The same definition evaluated one output row at a time.
+
+    ``rows`` lists ``(token, q_head)`` pairs; returns float64
+    ``[len(rows), d_v]``.  Used for spot checks at sizes where the full
+    result is too slow to form.
+    """
+    cu = _as_offsets(cu_seqlens)
+    rows = list(rows)
+    q_t = q
+    res = np.zeros((len(rows), np.shape(v)[2]), dtype=np.float64)
+    for r, (tok, h) in enumerate(rows):
+        s = int(np.searchsorted(np.asarray(cu), tok, side="right")) - 1
+        while cu[s + 1] <= tok:  # skip empty sequences sharing the offset
+            s += 1
+        a = cu[s]
+        i = tok - a
+        lo = 0 if window == 0 else max(0, i - window + 1)
+        g = kv_head_of(h, n_q_heads, n_kv_heads)
+        qi = _as_f64(q_t[tok, h, :])
+        kk = _as_f64(k[a + lo:a + i + 1, g, :])
+        vv = _as_f64(v[a + lo:a + i + 1, g, :])
+        sc = float(scale) * (kk @ qi)
+        e = np.exp(sc - sc.max())
+        res[r] = (e / e.sum()) @ vv
+    return res
+
+
+def visible_pairs(lengths: Sequence[int], window: int) -> int:
+    """Number of visible (query, key) pairs, summed over sequences."""
+    total = 0
+    for n in lengths:
+        total += int(visibility(int(n), int(n), window).sum()) if n else 0
+    return total

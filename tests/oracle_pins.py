@@ -1,0 +1,245 @@
+"""Pins of the FP64 oracle: checks against facts fixed outside the oracle.
+
+Each ``pin_*`` takes the oracle module (or a deliberately broken copy of it,
+see ``test_oracle_mutants.py``) and raises ``AssertionError`` when the module
+disagrees with:
+
+* hand-derived closed forms (``golden/worked_examples.json``),
+* the literal-loop brute force of ``bruteforce.py`` on tiny random inputs,
+* invariants of the definition (rows of P sum to one, W = 0 equals W >= L,
+  a one-token sequence returns its own V, W = 1 returns V, scale 0 gives the
+  mean of the visible V rows, constant V, convex hull, shift invariance in
+  K, packing and GQA replication),
+* torch's CPU float64 ``scaled_dot_product_attention`` as a second library
+  rendering of the causal case.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+from bruteforce import brute_attention
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "worked_examples.json")
+
+
+def _cu(lengths):
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    return cu
+
+
+def _rand(rng, lengths, hq, hkv, d):
+    t = sum(lengths)
+    return (rng.standard_normal((t, hq, d)), rng.standard_normal((t, hkv, d)),
+            rng.standard_normal((t, hkv, d)))
+
+
+def pin_golden(mod):
+    with open(GOLDEN) as f:
+        examples = json.load(f)["examples"]
+    for ex in examples:
+        got = mod.attention_varlen(np.array(ex["q"]), np.array(ex["k"]),
+                                   np.array(ex["v"]), ex["cu_seqlens"],
+                                   ex["n_q_heads"], ex["n_kv_heads"],
+                                   ex["scale"], ex["window"], workers=1)
+        want = np.array(ex["out"])
+        assert got.shape == want.shape, ex["name"]
+        err = np.max(np.abs(got - want))
+        assert err <= 1e-12, f"{ex['name']}: max err {err}"
+
+
+BRUTE_CASES = [
+    # lengths, hq, hkv, d, window, scale
+    ([5], 1, 1, 1, 0, 1.0),
+    ([7], 2, 1, 2, 0, 0.7),
+    ([9], 4, 2, 4, 2, 0.5),
+    ([6, 1, 0, 3], 4, 4, 8, 0, 0.35),
+    ([0, 2, 7], 4, 1, 4, 5, 1.3),
+    ([11], 2, 2, 3, 1, 0.9),
+    ([33], 4, 2, 8, 7, 0.25),
+    ([1, 1, 2], 2, 1, 2, 0, -0.8),
+    ([12, 5], 4, 2, 2, 12, 0.6),
+]
+
+
+def pin_bruteforce(mod):
+    for case_id, (lengths, hq, hkv, d, w, scale) in enumerate(BRUTE_CASES):
+        rng = np.random.default_rng(100 + case_id)
+        q, k, v = _rand(rng, lengths, hq, hkv, d)
+        cu = _cu(lengths)
+        want = np.array(brute_attention(q.tolist(), k.tolist(), v.tolist(), cu,
+                                        hq, hkv, scale, w)).reshape(q.shape[0], hq, d)
+        got = mod.attention_varlen(q, k, v, cu, hq, hkv, scale, w, workers=1)
+        err = np.max(np.abs(got - want)) if got.size else 0.0
+        assert err <= 1e-12, f"brute case {case_id}: max err {err}"
+        rows = [(t, h) for t in range(q.shape[0]) for h in range(hq)]
+        if rows:
+            got_r = mod.attention_rows(q, k, v, cu, hq, hkv, scale, w, rows)
+            want_r = np.array([want[t, h] for t, h in rows])
+            err_r = np.max(np.abs(got_r - want_r))
+            assert err_r <= 1e-12, f"brute case {case_id} rows: max err {err_r}"
+
+
+def pin_rows_sum_to_one(mod):
+    rng = np.random.default_rng(7)
+    for n, w in ((1, 0), (17, 0), (40, 3), (40, 40)):
+        q = rng.standard_normal((n, 8))
+        k = rng.standard_normal((n, 8)) * 3.0
+        p = mod.softmax_probs(q, k, 0.9, w)
+        assert np.max(np.abs(p.sum(axis=1) - 1.0)) <= 1e-12
+        i = np.arange(n)[:, None]
+        j = np.arange(n)[None, :]
+        masked = (j > i) | ((w > 0) & (j <= i - w))
+        assert np.all(p[masked] == 0.0)
+        assert np.all(p[~masked] > 0.0)
+
+
+def pin_window_zero_equals_long_window(mod):
+    rng = np.random.default_rng(8)
+    lengths = [23, 9]
+    q, k, v = _rand(rng, lengths, 4, 2, 8)
+    cu = _cu(lengths)
+    o0 = mod.attention_varlen(q, k, v, cu, 4, 2, 0.4, 0, workers=1)
+    for w in (23, 24, 1000):
+        ow = mod.attention_varlen(q, k, v, cu, 4, 2, 0.4, w, workers=1)
+        assert np.array_equal(o0, ow), f"window {w} differs from window 0"
+
+
+def pin_window_one_returns_v(mod):
+    rng = np.random.default_rng(9)
+    lengths = [13, 4]
+    q, k, v = _rand(rng, lengths, 4, 2, 8)
+    out = mod.attention_varlen(q, k, v, _cu(lengths), 4, 2, 1.1, 1, workers=1)
+    for h in range(4):
+        assert np.array_equal(out[:, h, :], v[:, h // 2, :])
+
+
+def pin_first_token_returns_v(mod):
+    rng = np.random.default_rng(10)
+    lengths = [1, 5, 1, 8, 3]
+    q, k, v = _rand(rng, lengths, 2, 1, 8)
+    cu = _cu(lengths)
+    out = mod.attention_varlen(q, k, v, cu, 2, 1, 0.8, 0, workers=1)
+    for s in range(len(lengths)):
+        for h in range(2):
+            assert np.array_equal(out[cu[s], h, :], v[cu[s], 0, :])
+
+
+def pin_scale_zero_mean(mod):
+    rng = np.random.default_rng(11)
+    lengths = [19]
+    q, k, v = _rand(rng, lengths, 2, 1, 4)
+    for w in (0, 4):
+        out = mod.attention_varlen(q, k, v, [0, 19], 2, 1, 0.0, w, workers=1)
+        for i in range(19):
+            lo = 0 if w == 0 else max(0, i - w + 1)
+            want = v[lo:i + 1, 0, :].mean(axis=0)
+            assert np.max(np.abs(out[i, 0] - want)) <= 1e-12
+            assert np.max(np.abs(out[i, 1] - want)) <= 1e-12
+
+
+def pin_constant_v_and_hull(mod):
+    rng = np.random.default_rng(12)
+    q, k, _ = _rand(rng, [21], 2, 1, 4)
+    row = np.array([0.5, -2.0, 3.25, 1e-3])
+    v = np.broadcast_to(row, (21, 1, 4)).copy()
+    out = mod.attention_varlen(q, k, v, [0, 21], 2, 1, 1.7, 0, workers=1)
+    assert np.max(np.abs(out - row)) <= 1e-12
+    v = rng.standard_normal((21, 1, 4))
+    out = mod.attention_varlen(q, k, v, [0, 21], 2, 1, 1.7, 5, workers=1)
+    for i in range(21):
+        vis = v[max(0, i - 4):i + 1, 0, :]
+        assert np.all(out[i, 0] <= vis.max(axis=0) + 1e-12)
+        assert np.all(out[i, 0] >= vis.min(axis=0) - 1e-12)
+
+
+def pin_k_shift_invariance(mod):
+    rng = np.random.default_rng(13)
+    q, k, v = _rand(rng, [25], 2, 1, 8)
+    base = mod.attention_varlen(q, k, v, [0, 25], 2, 1, 0.6, 6, workers=1)
+    shifted = mod.attention_varlen(q, k + rng.standard_normal(8), v, [0, 25],
+                                   2, 1, 0.6, 6, workers=1)
+    assert np.max(np.abs(base - shifted)) <= 1e-11
+
+
+def pin_packing_equals_separate(mod):
+    rng = np.random.default_rng(14)
+    lengths = [7, 0, 12, 1, 5]
+    q, k, v = _rand(rng, lengths, 4, 2, 8)
+    cu = _cu(lengths)
+    packed = mod.attention_varlen(q, k, v, cu, 4, 2, 0.45, 3, workers=1)
+    for s, n in enumerate(lengths):
+        a, b = cu[s], cu[s + 1]
+        alone = mod.attention_varlen(q[a:b], k[a:b], v[a:b], [0, n], 4, 2,
+                                     0.45, 3, workers=1)
+        assert np.max(np.abs(packed[a:b] - alone), initial=0.0) <= 1e-12
+
+
+def pin_gqa_equals_replicated(mod):
+    rng = np.random.default_rng(15)
+    lengths = [10, 6]
+    q, k, v = _rand(rng, lengths, 6, 2, 4)
+    cu = _cu(lengths)
+    gqa = mod.attention_varlen(q, k, v, cu, 6, 2, 0.5, 0, workers=1)
+    k_rep = np.repeat(k, 3, axis=1)  # head h reads kv head h // 3
+    v_rep = np.repeat(v, 3, axis=1)
+    mha = mod.attention_varlen(q, k_rep, v_rep, cu, 6, 6, 0.5, 0, workers=1)
+    assert np.max(np.abs(gqa - mha)) <= 1e-12
+
+
+def pin_sdpa_crosscheck(mod):
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(16)
+    n, hq, hkv, d = 37, 4, 1, 16
+    q, k, v = _rand(rng, [n], hq, hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    qt = torch.from_numpy(q).permute(1, 0, 2)  # [H, L, d]
+    kt = torch.from_numpy(np.repeat(k, hq, axis=1)).permute(1, 0, 2)
+    vt = torch.from_numpy(np.repeat(v, hq, axis=1)).permute(1, 0, 2)
+    ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                         scale=scale).permute(1, 0, 2).numpy()
+    got = mod.attention_varlen(q, k, v, [0, n], hq, hkv, scale, 0, workers=1)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+    w = 5
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    mask = (j <= i) & (j >= i - w + 1)
+    ref_w = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                           scale=scale).permute(1, 0, 2).numpy()
+    got_w = mod.attention_varlen(q, k, v, [0, n], hq, hkv, scale, w, workers=1)
+    assert np.max(np.abs(got_w - ref_w)) <= 1e-12
+
+
+def pin_parallel_equals_serial(mod):
+    rng = np.random.default_rng(17)
+    lengths = [30, 17, 0, 41]
+    q, k, v = _rand(rng, lengths, 4, 1, 8)
+    cu = _cu(lengths)
+    a = mod.attention_varlen(q, k, v, cu, 4, 1, 0.3, 0, workers=1)
+    b = mod.attention_varlen(q, k, v, cu, 4, 1, 0.3, 0, workers=4)
+    assert np.array_equal(a, b)
+
+
+ALL_PINS = [
+    pin_golden,
+    pin_bruteforce,
+    pin_rows_sum_to_one,
+    pin_window_zero_equals_long_window,
+    pin_window_one_returns_v,
+    pin_first_token_returns_v,
+    pin_scale_zero_mean,
+    pin_constant_v_and_hull,
+    pin_k_shift_invariance,
+    pin_packing_equals_separate,
+    pin_gqa_equals_replicated,
+    pin_sdpa_crosscheck,
+    pin_parallel_equals_serial,
+]

@@ -1,0 +1,128 @@
+"""The pins are strong enough: planted mistakes in a copy of the oracle fail.
+
+Each mutant is a private copy of ``oracle/attention.py`` with one plausible
+mistake (a wrong mask index, a dropped term, a transposed operand, a wrong
+head map...).  The real oracle passes every pin (``test_oracle.py``); each
+mutant must fail at least one.  The pristine copy is run through the same
+harness first so that a harness that catches nothing cannot score.
+"""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from oracle_pins import ALL_PINS
+
+ORACLE_PATH = os.path.join(os.path.dirname(os.path.dirname(
+    os.path.abspath(__file__))), "oracle", "attention.py")
+
+
+def fresh_copy(tag):
+    spec = importlib.util.spec_from_file_location(f"_oracle_copy_{tag}", ORACLE_PATH)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def failing_pins(mod):
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception as e:  # a crash also counts as caught
+            failed.append(f"{pin.__name__}:{type(e).__name__}")
+    return failed
+
+
+def _vis(op):
+    def visibility(n_rows, n_cols, window):
+        i = np.arange(n_rows)[:, None]
+        j = np.arange(n_cols)[None, :]
+        return op(i, j, window)
+    return visibility
+
+
+def _probs(variant):
+    def softmax_probs(q_h, k_g, scale, window, _v=variant):
+        q_h = np.asarray(q_h, dtype=np.float64)
+        k_g = np.asarray(k_g, dtype=np.float64)
+        n = q_h.shape[0]
+        vis = MUT_VIS_BASE(n, n, window)
+        if _v == "transposed":
+            s = scale * (k_g @ q_h.T)
+        elif _v == "no_scale":
+            s = q_h @ k_g.T
+        elif _v == "neg_scale":
+            s = -scale * (q_h @ k_g.T)
+        else:
+            s = scale * (q_h @ k_g.T)
+        if _v == "mask_as_zero":
+            s = np.where(vis, s, 0.0)
+        else:
+            s = np.where(vis, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        if _v == "no_normalise":
+            return e
+        if _v == "normalise_columns":
+            return e / e.sum(axis=0, keepdims=True)
+        return e / e.sum(axis=1, keepdims=True)
+    return softmax_probs
+
+
+def MUT_VIS_BASE(n_rows, n_cols, window):
+    i = np.arange(n_rows)[:, None]
+    j = np.arange(n_cols)[None, :]
+    vis = j <= i
+    if window > 0:
+        vis &= j >= i - window + 1
+    return vis
+
+
+def _no_isolation(mod):
+    base = mod.attention_varlen
+
+    def attention_varlen(q, k, v, cu_seqlens, hq, hkv, scale, window, workers=None):
+        cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+        return base(q, k, v, [0, cu[-1]], hq, hkv, scale, window, workers=workers)
+    return attention_varlen
+
+
+MUTANTS = {
+    "causal_excludes_self": ("visibility", _vis(
+        lambda i, j, w: (j < i) | ((i == 0) & (j == 0)) if w == 0 else
+        (j < i) & (j >= i - w + 1) | ((i == 0) & (j == 0)))),
+    "causal_lookahead_one": ("visibility", _vis(
+        lambda i, j, w: (j <= i + 1) & ((w == 0) | (j >= i - w + 1)))),
+    "window_one_too_wide": ("visibility", _vis(
+        lambda i, j, w: (j <= i) & ((w == 0) | (j >= i - w)))),
+    "window_one_too_narrow": ("visibility", _vis(
+        lambda i, j, w: (j <= i) & ((w == 0) | (j >= i - w + 2) | (j == i)))),
+    "no_mask": ("visibility", _vis(lambda i, j, w: np.ones_like(i + j, dtype=bool))),
+    "kv_head_modulo": ("kv_head_of", lambda h, hq, hkv: h % hkv),
+    "kv_head_zero": ("kv_head_of", lambda h, hq, hkv: 0),
+    "scores_transposed": ("softmax_probs", _probs("transposed")),
+    "scale_dropped": ("softmax_probs", _probs("no_scale")),
+    "scale_sign_flipped": ("softmax_probs", _probs("neg_scale")),
+    "masked_scores_zero_not_neg_inf": ("softmax_probs", _probs("mask_as_zero")),
+    "softmax_not_normalised": ("softmax_probs", _probs("no_normalise")),
+    "softmax_normalised_over_queries": ("softmax_probs", _probs("normalise_columns")),
+    "sequences_not_isolated": ("attention_varlen", None),
+}
+
+
+def test_pristine_copy_passes_every_pin():
+    assert failing_pins(fresh_copy("pristine")) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = fresh_copy(name)
+    attr, repl = MUTANTS[name]
+    if name == "sequences_not_isolated":
+        repl = _no_isolation(mod)
+    setattr(mod, attr, repl)
+    assert failing_pins(mod), f"mutant {name} passed every pin"

@@ -1,0 +1,66 @@
+"""Seeded generators and the work counter (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_prefill_attention_amd import measure, workloads
+
+VARLEN = "varlen16_gqa32q8kv_fp32q_fp16kv"
+
+
+def test_varlen_lengths_are_seeded_and_in_range():
+    w = workloads.WORKLOADS[VARLEN]
+    a = workloads.draw_lengths(w, np.random.default_rng(w.seed))
+    b = workloads.draw_lengths(w, np.random.default_rng(w.seed))
+    assert a == b and len(a) == 16
+    assert all(64 <= n <= 2048 for n in a)
+    assert a == [1674, 234, 420, 534, 424, 1654, 1789, 1219, 142, 250, 723,
+                 923, 1297, 1014, 589, 381]
+
+
+def test_make_inputs_deterministic_and_typed():
+    w = workloads.custom("t", [5, 0, 9], 4, 2, head_dim=16, q_dtype="fp32",
+                         kv_dtype="fp16", seed=3)
+    a = workloads.make_inputs(w)
+    b = workloads.make_inputs(w)
+    assert a["sha256"] == b["sha256"]
+    assert a["q"].dtype == torch.float32 and a["k"].dtype == torch.float16
+    assert tuple(a["q"].shape) == (14, 4, 16)
+    assert tuple(a["k"].shape) == (14, 2, 16)
+    assert a["cu_seqlens"].tolist() == [0, 5, 5, 14]
+    assert a["cu_seqlens"].dtype == torch.int32
+
+
+def test_outlier_count():
+    w = workloads.custom("o", [64], 4, 1, head_dim=128, seed=4,
+                         k_outlier_frac=0.01)
+    base = workloads.custom("b", [64], 4, 1, head_dim=128, seed=4)
+    k1 = workloads.make_inputs(w)["k"].float()
+    k0 = workloads.make_inputs(base)["k"].float()
+    changed = (k1 != k0).sum().item()
+    n = math.floor(0.01 * k0.numel())
+    # scaling by 30 can leave a value unchanged only if it was zero
+    assert changed == n
+
+
+@pytest.mark.parametrize("n,w", [(0, 0), (1, 0), (5, 0), (5, 1), (5, 3),
+                                 (5, 5), (5, 9), (64, 17), (130, 64)])
+def test_pair_count_closed_form_matches_brute_count(n, w):
+    assert measure.visible_pairs_one(n, w) == oracle.visible_pairs([n], w)
+
+
+def test_headline_flops():
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    f = measure.causal_flops(list(w.lengths), w.n_q_heads, w.head_dim, w.window)
+    assert f == 4 * 128 * 32 * (8192 * 8193 // 2)
+    assert abs(f - 5.498e11) / 5.498e11 < 1e-3
+
+
+def test_sample_rows_cover_edges():
+    rows = workloads.sample_rows([3, 0, 5], 4, 20, seed=1)
+    for r in [(0, 0), (0, 3), (2, 0), (3, 0), (7, 0), (7, 3)]:
+        assert r in rows
+    assert all(0 <= t < 8 and 0 <= h < 4 for t, h in rows)
