@@ -1,0 +1,244 @@
+"""Throughput of the causal prefill-attention kernel on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one ``attn_prefill`` call (one layer's causal prefill attention)
+over the workload's seeded synthetic batch, inputs resident in HBM.  W
+untimed warm-up steps, then exactly K timed steps bracketed by
+``torch.cuda.synchronize()``.  Prints ONE JSON line:
+
+* ``value``: causal TFLOP/s of the whole step (F / wall time per step),
+  F = 4 * head_dim * n_q_heads * (visible query-key pairs);
+* ``roofline``: the kernel's average launch duration from HIP events
+  recorded around every timed launch on the launch stream, the algorithmic
+  TFLOP/s it implies against the bf16 dense MFMA peak, and the HBM traffic
+  measured by rocprofv3 counters (from ``profiles/``, null when the kernel
+  source changed since the counters were taken);
+* ``cpu_baseline``: the FP64 CPU oracle timed on a bounded sample of the
+  same workload (a subset of the query heads, all tokens), scaled to the
+  same unit, with the number of threads it used.
+
+``--mode copy`` instead runs a plain device-to-device copy of known size;
+its rocprofv3 FETCH_SIZE / WRITE_SIZE readings calibrate the counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "prefill_fwd.hip"),
+    os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "prefill_params.h"),
+]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, inp, n_heads_sample: int):
+    """Times the oracle on the first ``n_heads_sample`` query heads."""
+    import oracle
+    from causal_prefill_attention_amd import measure
+
+    hs = max(1, min(n_heads_sample, w.n_q_heads))
+    n_kv = 1
+    if w.n_kv_heads > 1:
+        # whole GQA groups, so that every sampled head keeps its kv head
+        group = w.n_q_heads // w.n_kv_heads
+        n_kv = (hs + group - 1) // group
+        hs = n_kv * group
+    q = inp["q"][:, :hs]
+    k = inp["k"][:, :n_kv]
+    v = inp["v"][:, :n_kv]
+    threads = host_threads()
+    t0 = time.perf_counter()
+    oracle.attention_varlen(q, k, v, inp["cu_seqlens"], hs, n_kv, w.attn_scale,
+                            w.window, workers=threads)
+    dt = time.perf_counter() - t0
+    flops = measure.causal_flops(inp["lengths"], hs, w.head_dim, w.window)
+    jobs = hs * sum(1 for n in inp["lengths"] if n > 0)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(threads, jobs),
+        "kind": "oracle",
+        "sample": (f"{w.name}: {hs} of {w.n_q_heads} query heads, all "
+                   f"{sum(inp['lengths'])} tokens, numpy float64, {dt:.2f} s wall"),
+        "seconds": dt,
+    }
+
+
+def run_copy(args):
+    import torch
+
+    n = args.copy_mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n,
+                      "ms_per_copy": dt * 1e3, "GB/s": 2 * n / dt / 1e9}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="query heads of the workload the CPU oracle times "
+                         "(default: one per host thread)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["attn", "copy"], default="attn")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(prefill attention would shard by query head or by sequence "
+              "with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.mode == "copy":
+        run_copy(args)
+        return
+
+    from causal_prefill_attention_amd import binding, measure, workloads
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    lengths = inp["lengths"]
+    dev = torch.device("cuda:0")
+    q = inp["q"].to(dev)
+    k = inp["k"].to(dev)
+    v = inp["v"].to(dev)
+    cu = inp["cu_seqlens"].to(dev)
+    out = torch.empty(q.shape[0], w.n_q_heads, w.head_dim, dtype=torch.bfloat16,
+                      device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.attn_prefill(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads,
+                             w.head_dim, w.attn_scale, w.window, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, per-launch events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
+    avg_ms = sum(durs) / len(durs)
+
+    flops = measure.causal_flops(lengths, w.n_q_heads, w.head_dim, w.window)
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = measure.PEAK_BF16_TFLOPS
+    traffic = load_traffic(name)
+
+    line = {
+        "metric": "causal prefill attention TFLOP/s and % of bf16 MFMA peak "
+                  "(hd=128, MQA)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {
+            "workload": name,
+            "seq_lens": lengths if len(lengths) <= 16 else f"{len(lengths)} seqs",
+            "tokens": int(sum(lengths)),
+            "n_q_heads": w.n_q_heads,
+            "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim,
+            "sliding_window": w.window,
+            "q_dtype": w.q_dtype,
+            "kv_dtype": w.kv_dtype,
+            "k_outlier_frac": w.k_outlier_frac,
+            "scale": w.attn_scale,
+            "causal_flops": flops,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": round(peak, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "kernel_min_us": round(durs[0] * 1e3, 2),
+            "algorithmic_bytes": measure.algorithmic_bytes(
+                lengths, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads or host_threads())
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,13 +6,12 @@ with ctypes.  ``workloads`` draws seeded synthetic inputs and ``measure``
 counts algorithmic work.  There is no CPU fallback: if the library is
 missing, calling it raises.
 """
+import importlib
 
 __all__ = ["binding", "workloads", "measure"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-
-        return binding
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,153 @@
+"""ctypes binding of libattn_prefill.so -- argument marshalling only.
+
+Torch provides device memory and the stream; every step of the attention
+runs in the library's HIP kernels.  There is no CPU path: if the library is
+missing or a tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libattn_prefill.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_HIP = 3
+
+ATTN_BF16 = 0
+ATTN_FP16 = 1
+ATTN_FP32 = 2
+
+#: Every symbol include/attn_prefill.h declares.
+EXPORTS = ("attn_prefill", "attn_prefill_status_string",
+           "attn_prefill_last_error", "attn_prefill_supported_head_dims",
+           "attn_prefill_version")
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("n_tokens", ctypes.c_int64),
+                ("token_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
+
+
+class AttnSeqlens(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("n_seqs", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32)]
+
+
+class AttnPrefillError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn_prefill failed ({status}): {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads the HIP library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m causal_prefill_attention_amd.build_lib` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_prefill.argtypes = [
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnSeqlens), ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_prefill_status_string.restype = ctypes.c_char_p
+    lib.attn_prefill_status_string.argtypes = [ctypes.c_int]
+    lib.attn_prefill_last_error.restype = ctypes.c_char_p
+    lib.attn_prefill_last_error.argtypes = []
+    lib.attn_prefill_supported_head_dims.restype = ctypes.c_int
+    lib.attn_prefill_supported_head_dims.argtypes = [
+        ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
+    lib.attn_prefill_version.restype = ctypes.c_int
+    lib.attn_prefill_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().attn_prefill_last_error().decode()
+
+
+def supported_head_dims():
+    lib = load_library()
+    n = lib.attn_prefill_supported_head_dims(None, 0)
+    arr = (ctypes.c_int32 * n)()
+    lib.attn_prefill_supported_head_dims(arr, n)
+    return list(arr)
+
+
+def call_raw(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
+             seqlens: AttnSeqlens, n_q_heads: int, n_kv_heads: int,
+             head_dim: int, scale: float, sliding_window: int,
+             stream: Optional[int] = None) -> int:
+    """Calls the C entry point with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                            ctypes.byref(out), ctypes.byref(seqlens),
+                            int(n_q_heads), int(n_kv_heads), int(head_dim),
+                            float(scale), int(sliding_window),
+                            ctypes.c_void_p(stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_FP16,
+             torch.float32: ATTN_FP32}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def describe(t) -> AttnTensor:
+    """Descriptor of a [T, H, d] device tensor with a contiguous last axis."""
+    if not t.is_cuda:
+        raise ValueError("tensor is not on the GPU (there is no CPU path)")
+    if t.dim() != 3:
+        raise ValueError(f"expected [tokens, heads, head_dim], got {tuple(t.shape)}")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError("the head_dim axis must be contiguous")
+    return AttnTensor(t.data_ptr() if t.numel() else None, _dtype_code(t), 0,
+                      t.shape[0], t.stride(0), t.stride(1))
+
+
+def attn_prefill(q, k, v, out, cu_seqlens, n_q_heads: int, n_kv_heads: int,
+                 head_dim: int, scale: float, sliding_window: int = 0,
+                 stream=None) -> None:
+    """Runs the HIP kernel; ``out`` is written in place.
+
+    q: [T, n_q_heads, head_dim] bf16/fp32; k, v: [T, n_kv_heads, head_dim]
+    bf16/fp16; out: [T, n_q_heads, head_dim] bf16; cu_seqlens: int32 device
+    tensor of n_seqs + 1 offsets.  ``stream`` defaults to torch's current
+    stream on q's device.
+    """
+    import torch
+
+    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be an int32 GPU tensor")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2 or cu_seqlens.stride(0) != 1:
+        raise ValueError("cu_seqlens must be a contiguous 1-D tensor of n_seqs + 1")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    seq = AttnSeqlens(cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, 0)
+    status = call_raw(describe(q), describe(k), describe(v), describe(out), seq,
+                      n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
+                      handle)
+    if status != ATTN_OK:
+        raise AttnPrefillError(status, last_error())

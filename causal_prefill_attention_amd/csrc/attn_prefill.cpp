@@ -1,0 +1,235 @@
+// C ABI of the prefill-attention library: argument checks, dispatch, errors.
+//
+// Every check runs on the host before the first HIP call, so a bad argument
+// never reaches the device and every error path is testable without a GPU.
+// Nothing is allocated and nothing synchronises (unless the debug variable
+// ATTN_PREFILL_VALIDATE=1 asks for a host check of cu_seqlens).
+#include "attn_prefill.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime_api.h>
+
+#include "prefill_params.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+const int32_t kHeadDims[] = {128};
+
+bool head_dim_supported(int32_t d) {
+  for (int32_t x : kHeadDims)
+    if (x == d) return true;
+  return false;
+}
+
+int64_t elem_bytes(int32_t dtype) { return dtype == ATTN_FP32 ? 4 : 2; }
+
+bool dtype_known(int32_t dtype) {
+  return dtype == ATTN_BF16 || dtype == ATTN_FP16 || dtype == ATTN_FP32;
+}
+
+// Byte range [lo, hi) touched by a tensor of n_heads x head_dim per token.
+struct Extent {
+  uintptr_t lo, hi;
+};
+
+Extent extent_of(const attn_tensor* t, int32_t n_heads, int32_t head_dim) {
+  const int64_t last = (t->n_tokens - 1) * t->token_stride +
+                       (int64_t)(n_heads - 1) * t->head_stride + head_dim;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(t->data);
+  return {lo, lo + (uintptr_t)(last * elem_bytes(t->dtype))};
+}
+
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks one tensor descriptor; `what` names it in messages.
+int check_tensor(const attn_tensor* t, const char* what, int32_t n_heads, int32_t head_dim) {
+  if (t == nullptr) return fail(ATTN_ERR_INVALID_ARG, "%s: descriptor is NULL", what);
+  if (!dtype_known(t->dtype))
+    return fail(ATTN_ERR_INVALID_ARG, "%s: unknown dtype code %d", what, (int)t->dtype);
+  if (t->reserved != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: reserved field must be 0", what);
+  if (t->n_tokens < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: n_tokens %lld < 0", what, (long long)t->n_tokens);
+  if (t->n_tokens > INT32_MAX)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: n_tokens %lld exceeds int32 offsets", what,
+                (long long)t->n_tokens);
+  if (t->n_tokens == 0) return ATTN_OK;
+  if (t->data == nullptr) return fail(ATTN_ERR_INVALID_ARG, "%s: data is NULL", what);
+  if (t->token_stride < 0 || t->head_stride < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: negative stride", what);
+  // Head vectors must not overlap: token-major or head-major nesting.
+  const int64_t T = t->n_tokens, H = n_heads, d = head_dim;
+  const int64_t ts = t->token_stride, hs = t->head_stride;
+  const bool token_major = (H == 1 || hs >= d) && (T == 1 || ts >= (H - 1) * hs + d);
+  const bool head_major = (T == 1 || ts >= d) && (H == 1 || hs >= (T - 1) * ts + d);
+  if (!token_major && !head_major)
+    return fail(ATTN_ERR_INVALID_ARG,
+                "%s: strides (token %lld, head %lld) overlap head vectors of %d x %d",
+                what, (long long)ts, (long long)hs, (int)H, (int)d);
+  const int64_t eb = elem_bytes(t->dtype);
+  if ((reinterpret_cast<uintptr_t>(t->data) & 15u) != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: data pointer is not 16-byte aligned", what);
+  if ((ts * eb) % 16 != 0 || (hs * eb) % 16 != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: strides are not multiples of 16 bytes", what);
+  return ATTN_OK;
+}
+
+int debug_validate_offsets(const attn_seqlens* cu, int64_t n_tokens, hipStream_t stream) {
+  std::vector<int32_t> host((size_t)cu->n_seqs + 1);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess)
+    e = hipMemcpy(host.data(), cu->data, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess)
+    return fail(ATTN_ERR_HIP, "ATTN_PREFILL_VALIDATE: reading cu_seqlens failed: %s",
+                hipGetErrorString(e));
+  if (host[0] != 0) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", host[0]);
+  for (size_t i = 1; i < host.size(); ++i)
+    if (host[i] < host[i - 1])
+      return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens decreases at index %zu", i);
+  if (host.back() != n_tokens)
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens[n_seqs] = %d, expected n_tokens = %lld",
+                host.back(), (long long)n_tokens);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                 const attn_tensor* out, const attn_seqlens* cu_seqlens,
+                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                 int32_t sliding_window, attn_stream_t stream) {
+  g_last_error.clear();
+  if (n_q_heads < 1 || n_kv_heads < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
+                (int)n_q_heads, (int)n_kv_heads);
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                (int)n_q_heads, (int)n_kv_heads);
+  if (head_dim < 1) return fail(ATTN_ERR_INVALID_ARG, "head_dim %d < 1", (int)head_dim);
+  if (!head_dim_supported(head_dim))
+    return fail(ATTN_ERR_UNSUPPORTED, "no kernel for head_dim %d (supported: 128)",
+                (int)head_dim);
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
+  if (sliding_window < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "sliding_window %d < 0 (0 = off)", (int)sliding_window);
+  int rc;
+  if ((rc = check_tensor(q, "q", n_q_heads, head_dim)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(k, "k", n_kv_heads, head_dim)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(v, "v", n_kv_heads, head_dim)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(out, "out", n_q_heads, head_dim)) != ATTN_OK) return rc;
+  if (q->dtype != ATTN_BF16 && q->dtype != ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "q dtype must be BF16 or FP32");
+  if (k->dtype != v->dtype) return fail(ATTN_ERR_UNSUPPORTED, "k and v dtypes differ");
+  if (k->dtype != ATTN_BF16 && k->dtype != ATTN_FP16)
+    return fail(ATTN_ERR_UNSUPPORTED, "k/v dtype must be BF16 or FP16");
+  if (out->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "out dtype must be BF16");
+  const int64_t T = q->n_tokens;
+  if (k->n_tokens != T || v->n_tokens != T || out->n_tokens != T)
+    return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: q %lld k %lld v %lld out %lld",
+                (long long)T, (long long)k->n_tokens, (long long)v->n_tokens,
+                (long long)out->n_tokens);
+  if (cu_seqlens == nullptr) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (cu_seqlens->n_seqs < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "n_seqs %d < 1", (int)cu_seqlens->n_seqs);
+  if (cu_seqlens->data == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens data is NULL");
+  if (cu_seqlens->max_seqlen < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "max_seqlen %d < 0", (int)cu_seqlens->max_seqlen);
+  if (T == 0) return ATTN_OK;  // nothing to compute or write
+  const Extent eo = extent_of(out, n_q_heads, head_dim);
+  if (overlaps(eo, extent_of(q, n_q_heads, head_dim)) ||
+      overlaps(eo, extent_of(k, n_kv_heads, head_dim)) ||
+      overlaps(eo, extent_of(v, n_kv_heads, head_dim)))
+    return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
+
+  const int bm = attnp::prefill_block_m(head_dim);
+  const int64_t slots = (T + bm - 1) / bm + cu_seqlens->n_seqs;
+  const int64_t blocks = slots * n_q_heads;
+  if (slots > INT32_MAX || blocks * 256 >= ((int64_t)1 << 32))
+    return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large",
+                (long long)blocks);
+
+  const char* dbg = getenv("ATTN_PREFILL_VALIDATE");
+  if (dbg != nullptr && dbg[0] == '1') {
+    if ((rc = debug_validate_offsets(cu_seqlens, T, stream)) != ATTN_OK) return rc;
+  }
+
+  attnp::PrefillParams p;
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.out = out->data;
+  p.cu_seqlens = cu_seqlens->data;
+  p.q_ts = q->token_stride;
+  p.q_hs = q->head_stride;
+  p.k_ts = k->token_stride;
+  p.k_hs = k->head_stride;
+  p.v_ts = v->token_stride;
+  p.v_hs = v->head_stride;
+  p.o_ts = out->token_stride;
+  p.o_hs = out->head_stride;
+  p.n_tokens = (int32_t)T;
+  p.n_seqs = cu_seqlens->n_seqs;
+  p.n_q_heads = n_q_heads;
+  p.group = n_q_heads / n_kv_heads;
+  p.window = sliding_window;
+  p.tile_slots = (int32_t)slots;
+  const float log2e = 1.4426950408889634f;
+  if (scale == 0.f) {
+    p.score_mult = 1.f;  // Q is zeroed, every visible score is 0
+    p.q_mult = 0.f;
+  } else {
+    p.score_mult = fabsf(scale) * log2e;
+    p.q_mult = scale < 0.f ? -1.f : 1.f;
+  }
+  const hipError_t e = attnp::launch_prefill(p, head_dim, (attnp::DType)q->dtype,
+                                             (attnp::DType)k->dtype,
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+const char* attn_prefill_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: argument outside the contract";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: no kernel for this configuration";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_prefill_last_error(void) { return g_last_error.c_str(); }
+
+int attn_prefill_supported_head_dims(int32_t* dims, int32_t cap) {
+  const int n = (int)(sizeof(kHeadDims) / sizeof(kHeadDims[0]));
+  for (int i = 0; i < n && i < cap && dims != nullptr; ++i) dims[i] = kHeadDims[i];
+  return n;
+}
+
+int attn_prefill_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal interface between the C ABI host code and the HIP kernels.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace attnp {
+
+enum DType : int32_t { kBF16 = 0, kFP16 = 1, kFP32 = 2 };
+
+// Everything one launch needs; passed to the kernel by value.  Strides are
+// in elements of the tensor's own dtype.
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const int32_t* cu_seqlens;  // device, n_seqs + 1 entries
+  int64_t q_ts, q_hs;         // token / head strides
+  int64_t k_ts, k_hs;
+  int64_t v_ts, v_hs;
+  int64_t o_ts, o_hs;
+  int32_t n_tokens;           // T (offsets are clamped into [0, T])
+  int32_t n_seqs;
+  int32_t n_q_heads;
+  int32_t group;              // n_q_heads / n_kv_heads
+  int32_t window;             // 0 = off
+  int32_t tile_slots;         // q-tile slots in the grid (>= real tiles)
+  float score_mult;           // log2(e) * |scale|, or 1 when scale == 0
+  float q_mult;               // +1, -1 or 0: sign of scale folded into Q
+};
+
+// Rows of queries per workgroup for a head size (the grid is sized with it).
+int prefill_block_m(int head_dim);
+
+// Launches the kernel for (head_dim, q dtype, kv dtype) on `stream`.
+// Returns hipErrorInvalidValue if no instantiation exists.
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
+                          DType kv_dtype, hipStream_t stream);
+
+}  // namespace attnp

@@ -1,0 +1,135 @@
+/*
+ * attn_prefill.h -- C ABI of the MI355X (gfx950) causal prefill-attention
+ * library (libattn_prefill.so).  Plain C: no C++ or torch types cross it.
+ *
+ * Operation (one call = one layer's prefill attention over a packed batch):
+ *
+ *   for every sequence s, query token i of s, query head h:
+ *     g        = h / (n_q_heads / n_kv_heads)          (consecutive GQA groups)
+ *     visible  = { j in s : j <= i  and  (W == 0  or  j >= i - W + 1) }
+ *     out[i,h] = sum_{j in visible} softmax_j(scale * q[i,h] . k[j,g]) * v[j,g]
+ *
+ * Sources on the pages:
+ *   - causal bound kv_end = min(q_pos + 1, seq_len) and online softmax: the
+ *     fused MLA prefill kernel in atlas PR #69 (its fix and re-audit commits);
+ *   - scale passed by the caller, sliding window passed as a width with
+ *     0 = off, head_dim explicit so that a 128-d head is never read with a
+ *     256-d stride: the cache-skip MLA prefill fix in atlas PR #69;
+ *   - the window keeps the W most recent keys (an exact recent ring): m40-llm
+ *     AGENTS.md, "Current Progress";
+ *   - packed variable-length prefill over cumulative offsets, GQA, FP16
+ *     storage with FP32 compute, Q in FP32 and K/V in FP16: m40-llm
+ *     AGENTS.md, "Project Snapshot" and the varlen-batch task under
+ *     "Current Tasks";
+ *   - fail loudly instead of falling back to a kernel of another head size:
+ *     the ensure! guard commits of atlas PR #69.
+ *
+ * Layouts.  Every tensor is [n_tokens, n_heads, head_dim] addressed as
+ *   data + token * token_stride + head * head_stride + c      (c < head_dim)
+ * in ELEMENTS of the tensor's dtype; the head_dim axis is contiguous.  Token-
+ * major ([T, H, d]) and head-major ([H, T, d]) layouts are both accepted.
+ * Sequences are packed back to back along the token axis; sequence s owns
+ * tokens [cu_seqlens[s], cu_seqlens[s+1]).
+ *
+ * Precision.  Q (bf16 or fp32) and K/V (bf16 or fp16) are rounded to bf16
+ * (round to nearest even) when loaded; both contractions run on bf16 MFMA
+ * with fp32 accumulation; softmax statistics are fp32; out is bf16 (RNE).
+ *
+ * Ownership and ordering.  The caller owns every buffer; the library keeps
+ * no pointer after the call returns and allocates nothing.  The call is
+ * asynchronous on `stream` (NULL = the null stream): it performs no host
+ * synchronisation, no device-to-host copy and no host read of cu_seqlens,
+ * so it may be captured in a HIP graph.  `out` must not overlap q, k or v.
+ *
+ * Errors.  Every argument check runs on the host before any HIP call; a
+ * failing check returns its status and leaves a message for
+ * attn_prefill_last_error().  There is no fallback to another head size,
+ * dtype or to the CPU.  cu_seqlens lives on the device and is not read by
+ * the host: the kernel clamps every offset into [0, n_tokens] and treats a
+ * negative-length sequence as empty, so malformed offsets give wrong output
+ * but no out-of-bounds access.  Setting ATTN_PREFILL_VALIDATE=1 in the
+ * environment adds a debug-only host check of cu_seqlens that synchronises
+ * the stream (never use it when timing or capturing).
+ */
+#ifndef ATTN_PREFILL_H
+#define ATTN_PREFILL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARG 1 /* argument outside the contract            */
+#define ATTN_ERR_UNSUPPORTED 2 /* valid, but no kernel for it (head_dim,   */
+                               /* dtype pair, alignment, grid size)        */
+#define ATTN_ERR_HIP 3         /* launch or runtime error from HIP         */
+
+/* element types */
+#define ATTN_BF16 0
+#define ATTN_FP16 1
+#define ATTN_FP32 2
+
+/* Same type as hipStream_t; declared here so that the header needs no HIP
+ * include. */
+typedef struct ihipStream_t* attn_stream_t;
+
+/* One device tensor [n_tokens, n_heads, head_dim] (n_heads and head_dim are
+ * the call's arguments).  Strides are in elements and must be >= 0; the
+ * head vectors of different (token, head) pairs must not overlap.  data must
+ * be 16-byte aligned and token_stride / head_stride must be multiples of
+ * 16 bytes, else ATTN_ERR_UNSUPPORTED. */
+typedef struct {
+  void* data;           /* device pointer, caller-owned; may be NULL if
+                           n_tokens == 0                                   */
+  int32_t dtype;        /* q: BF16 | FP32;  k, v: BF16 | FP16 (equal);
+                           out: BF16                                       */
+  int32_t reserved;     /* must be 0                                       */
+  int64_t n_tokens;     /* T; must agree across q, k, v and out            */
+  int64_t token_stride; /* elements between consecutive tokens             */
+  int64_t head_stride;  /* elements between consecutive heads              */
+} attn_tensor;
+
+/* Packed sequence offsets. */
+typedef struct {
+  const int32_t* data;  /* DEVICE int32[n_seqs + 1]: data[0] = 0,
+                           non-decreasing, data[n_seqs] = n_tokens         */
+  int32_t n_seqs;       /* >= 1                                            */
+  int32_t max_seqlen;   /* optional hint (0 = unknown); unused today       */
+} attn_seqlens;
+
+/* Causal (optionally sliding-window) prefill attention, see above.
+ *   n_q_heads >= 1, n_kv_heads >= 1, n_q_heads % n_kv_heads == 0
+ *   head_dim: one of attn_prefill_supported_head_dims() (128)
+ *   scale: finite (0 and negative values allowed), applied to q.k before
+ *          masking and softmax
+ *   sliding_window: 0 = off, W > 0 = the W most recent keys including the
+ *          query itself, < 0 = ATTN_ERR_INVALID_ARG
+ * Returns ATTN_OK or an error status. */
+int attn_prefill(const attn_tensor* q, const attn_tensor* k,
+                 const attn_tensor* v, const attn_tensor* out,
+                 const attn_seqlens* cu_seqlens, int32_t n_q_heads,
+                 int32_t n_kv_heads, int32_t head_dim, float scale,
+                 int32_t sliding_window, attn_stream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* attn_prefill_status_string(int status);
+
+/* Detail message of the calling thread's last failing call ("" if none).
+ * The pointer stays valid until the thread's next call into the library. */
+const char* attn_prefill_last_error(void);
+
+/* Writes up to `cap` supported head_dim values into `dims` (may be NULL when
+ * cap == 0) and returns how many exist. */
+int attn_prefill_supported_head_dims(int32_t* dims, int32_t cap);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int attn_prefill_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_PREFILL_H */

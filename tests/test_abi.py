@@ -1,0 +1,185 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+and rejects every bad argument on the host before any HIP call.
+
+Descriptors here carry fake, never-dereferenced device addresses: each case
+fails a host check, so no kernel is launched and no GPU is needed.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from causal_prefill_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_prefill.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_head_dims():
+    lib = B.load_library()
+    for code in (B.ATTN_OK, B.ATTN_ERR_INVALID_ARG, B.ATTN_ERR_UNSUPPORTED,
+                 B.ATTN_ERR_HIP, 99):
+        assert lib.attn_prefill_status_string(code)
+    assert B.supported_head_dims() == [128]
+    assert lib.attn_prefill_version() >= 100
+
+
+def tens(addr, dtype, n, heads, d=128, ts=None, hs=None):
+    hs = d if hs is None else hs
+    ts = heads * hs if ts is None else ts
+    return B.AttnTensor(addr, dtype, 0, n, ts, hs)
+
+
+def base_args(n=256, hq=32, hkv=1, d=128):
+    q = tens(FAKE, B.ATTN_BF16, n, hq, d)
+    k = tens(FAKE + (1 << 30), B.ATTN_BF16, n, hkv, d)
+    v = tens(FAKE + (2 << 30), B.ATTN_BF16, n, hkv, d)
+    o = tens(FAKE + (3 << 30), B.ATTN_BF16, n, hq, d)
+    s = B.AttnSeqlens(FAKE + (4 << 30), 1, 0)
+    return dict(q=q, k=k, v=v, out=o, seqlens=s, n_q_heads=hq, n_kv_heads=hkv,
+                head_dim=d, scale=1 / math.sqrt(d), sliding_window=0)
+
+
+def call(**kw):
+    return B.call_raw(kw["q"], kw["k"], kw["v"], kw["out"], kw["seqlens"],
+                      kw["n_q_heads"], kw["n_kv_heads"], kw["head_dim"],
+                      kw["scale"], kw["sliding_window"], None)
+
+
+def with_(a, **kw):
+    b = dict(a)
+    b.update(kw)
+    return b
+
+
+def mutate(t, **kw):
+    c = B.AttnTensor.from_buffer_copy(t)
+    for k, val in kw.items():
+        setattr(c, k, val)
+    return c
+
+
+BAD = [
+    # (name, mutation of base_args, expected status, message fragment)
+    ("zero_q_heads", lambda a: with_(a, n_q_heads=0), B.ATTN_ERR_INVALID_ARG, "n_q_heads"),
+    ("zero_kv_heads", lambda a: with_(a, n_kv_heads=0), B.ATTN_ERR_INVALID_ARG, "n_kv_heads"),
+    ("heads_not_multiple", lambda a: with_(a, n_q_heads=6, n_kv_heads=4),
+     B.ATTN_ERR_INVALID_ARG, "multiple"),
+    ("head_dim_256_unsupported", lambda a: with_(a, head_dim=256),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 256"),
+    ("head_dim_64_unsupported", lambda a: with_(a, head_dim=64),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 64"),
+    ("head_dim_zero", lambda a: with_(a, head_dim=0), B.ATTN_ERR_INVALID_ARG, "head_dim"),
+    ("scale_nan", lambda a: with_(a, scale=float("nan")), B.ATTN_ERR_INVALID_ARG, "scale"),
+    ("scale_inf", lambda a: with_(a, scale=float("inf")), B.ATTN_ERR_INVALID_ARG, "scale"),
+    ("window_negative", lambda a: with_(a, sliding_window=-1),
+     B.ATTN_ERR_INVALID_ARG, "sliding_window"),
+    ("q_null_data", lambda a: with_(a, q=mutate(a["q"], data=None)),
+     B.ATTN_ERR_INVALID_ARG, "q: data"),
+    ("k_bad_dtype", lambda a: with_(a, k=mutate(a["k"], dtype=7)),
+     B.ATTN_ERR_INVALID_ARG, "dtype"),
+    ("reserved_nonzero", lambda a: with_(a, v=mutate(a["v"], reserved=1)),
+     B.ATTN_ERR_INVALID_ARG, "reserved"),
+    ("q_fp16_unsupported", lambda a: with_(a, q=mutate(a["q"], dtype=B.ATTN_FP16)),
+     B.ATTN_ERR_UNSUPPORTED, "q dtype"),
+    ("kv_fp32_unsupported", lambda a: with_(a, k=mutate(a["k"], dtype=B.ATTN_FP32),
+                                            v=mutate(a["v"], dtype=B.ATTN_FP32)),
+     B.ATTN_ERR_UNSUPPORTED, "k/v dtype"),
+    ("kv_dtype_mismatch", lambda a: with_(a, k=mutate(a["k"], dtype=B.ATTN_FP16)),
+     B.ATTN_ERR_UNSUPPORTED, "differ"),
+    ("out_fp32_unsupported", lambda a: with_(a, out=mutate(a["out"], dtype=B.ATTN_FP32)),
+     B.ATTN_ERR_UNSUPPORTED, "out dtype"),
+    ("token_count_mismatch", lambda a: with_(a, v=mutate(a["v"], n_tokens=255)),
+     B.ATTN_ERR_INVALID_ARG, "n_tokens differ"),
+    ("negative_tokens", lambda a: with_(a, q=mutate(a["q"], n_tokens=-1)),
+     B.ATTN_ERR_INVALID_ARG, "n_tokens"),
+    ("too_many_tokens", lambda a: with_(a, q=mutate(a["q"], n_tokens=1 << 31)),
+     B.ATTN_ERR_INVALID_ARG, "int32"),
+    ("negative_stride", lambda a: with_(a, k=mutate(a["k"], token_stride=-128)),
+     B.ATTN_ERR_INVALID_ARG, "negative stride"),
+    ("overlapping_heads", lambda a: with_(a, q=mutate(a["q"], head_stride=64)),
+     B.ATTN_ERR_INVALID_ARG, "overlap head vectors"),
+    ("overlapping_tokens", lambda a: with_(a, q=mutate(a["q"], token_stride=31 * 128)),
+     B.ATTN_ERR_INVALID_ARG, "overlap head vectors"),
+    ("misaligned_pointer", lambda a: with_(a, q=mutate(a["q"], data=FAKE + 2)),
+     B.ATTN_ERR_UNSUPPORTED, "aligned"),
+    ("stride_not_16_bytes", lambda a: with_(a, k=mutate(a["k"], token_stride=132)),
+     B.ATTN_ERR_UNSUPPORTED, "16 bytes"),
+    ("seqlens_null_data", lambda a: with_(a, seqlens=B.AttnSeqlens(None, 1, 0)),
+     B.ATTN_ERR_INVALID_ARG, "cu_seqlens data"),
+    ("seqlens_zero_seqs", lambda a: with_(a, seqlens=B.AttnSeqlens(FAKE, 0, 0)),
+     B.ATTN_ERR_INVALID_ARG, "n_seqs"),
+    ("seqlens_negative_hint", lambda a: with_(a, seqlens=B.AttnSeqlens(FAKE, 1, -5)),
+     B.ATTN_ERR_INVALID_ARG, "max_seqlen"),
+    ("out_aliases_q", lambda a: with_(a, out=mutate(a["out"], data=a["q"].data + 256)),
+     B.ATTN_ERR_INVALID_ARG, "overlaps"),
+    ("out_aliases_k", lambda a: with_(a, out=mutate(a["out"], data=a["k"].data)),
+     B.ATTN_ERR_INVALID_ARG, "overlaps"),
+]
+
+
+@pytest.mark.parametrize("name,mut,status,frag", BAD, ids=[b[0] for b in BAD])
+def test_bad_argument_rejected_on_host(name, mut, status, frag):
+    rc = call(**mut(base_args()))
+    assert rc == status, (rc, B.last_error())
+    assert frag in B.last_error(), B.last_error()
+
+
+def test_null_descriptors_rejected():
+    lib = B.load_library()
+    a = base_args()
+    rc = lib.attn_prefill(None, ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                          ctypes.byref(a["out"]), ctypes.byref(a["seqlens"]),
+                          32, 1, 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "q: descriptor" in B.last_error()
+    rc = lib.attn_prefill(ctypes.byref(a["q"]), ctypes.byref(a["k"]),
+                          ctypes.byref(a["v"]), ctypes.byref(a["out"]), None,
+                          32, 1, 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "cu_seqlens" in B.last_error()
+
+
+def test_empty_batch_is_a_no_op_without_hip():
+    a = base_args(n=0)
+    for key in ("q", "k", "v", "out"):
+        a[key] = mutate(a[key], data=None)
+    assert call(**a) == B.ATTN_OK
+    assert B.last_error() == ""
+
+
+def test_head_major_layout_accepted_by_checks():
+    # [H, T, d] strides pass the overlap check; the call then fails on the
+    # next check (a misaligned out pointer) before any HIP call.
+    a = base_args(n=64, hq=4)
+    a["q"] = mutate(a["q"], token_stride=128, head_stride=64 * 128)
+    a["out"] = mutate(a["out"], data=a["out"].data + 2)
+    rc = call(**a)
+    assert rc == B.ATTN_ERR_UNSUPPORTED and "out: data pointer" in B.last_error()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(4, 1, 128, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        B.attn_prefill(q, q, q, q.clone(), cu, 1, 1, 128, 0.1)

@@ -1,0 +1,296 @@
+"""Parity of the HIP kernel (through the C ABI) with the FP64 oracle.
+
+Bar (on the bf16 outputs, against the unrounded float64 oracle):
+    max |gpu - oracle| <= 2e-2   and   mean |gpu - oracle| <= 2e-3
+Every comparison prints the fraction of each bar it used.
+
+Sizes: every configuration that the oracle finishes in seconds is compared
+element by element (several 128-row query tiles, ragged tails, packed
+batches); the full-size workloads are compared on a seeded sample of
+(token, head) rows that the oracle evaluates one by one, from the same
+launch the benchmark times.
+"""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_prefill_attention_amd import binding, workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+LOG = os.environ.get("ATTN_PARITY_LOG")
+
+
+def _announce(msg):
+    sys.stdout.write(f"\n[case] {msg}\n")
+    sys.stdout.flush()
+
+
+def _record(name, max_err, mean_err, n):
+    line = {"case": name, "max_abs": max_err, "mean_abs": mean_err,
+            "max_frac": max_err / MAX_ABS, "mean_frac": mean_err / MEAN_ABS,
+            "elements": n}
+    sys.stdout.write(f"[parity] {json.dumps(line)}\n")
+    sys.stdout.flush()
+    if LOG:
+        with open(LOG, "a") as f:
+            f.write(json.dumps(line) + "\n")
+
+
+def check(name, got, want):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == want.shape
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    err = np.abs(got - want)
+    max_err = float(err.max()) if err.size else 0.0
+    mean_err = float(err.mean()) if err.size else 0.0
+    _record(name, max_err, mean_err, int(err.size))
+    assert max_err <= MAX_ABS, f"{name}: max abs {max_err}"
+    assert mean_err <= MEAN_ABS, f"{name}: mean abs {mean_err}"
+
+
+def run_gpu(inp, hq, hkv, d, scale, window, out=None):
+    dev = torch.device("cuda:0")
+    q = inp["q"].to(dev)
+    k = inp["k"].to(dev)
+    v = inp["v"].to(dev)
+    cu = inp["cu_seqlens"].to(dev)
+    if out is None:
+        out = torch.empty(q.shape[0], hq, d, dtype=torch.bfloat16, device=dev)
+    binding.attn_prefill(q, k, v, out, cu, hq, hkv, d, scale, window)
+    torch.cuda.synchronize()
+    return out
+
+
+def to64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+# ------------------------------------------------------- full-oracle parity
+FULL = [
+    # name, lengths, hq, hkv, window, q dtype, kv dtype, scale
+    ("causal_128tok_4q1kv", None, 0, 0, 0, None, None, None),
+    ("mla_2048tok_32q1kv", None, 0, 0, 0, None, None, None),
+    ("window256_1100tok_32q1kv", [1100], 32, 1, 256, "bf16", "bf16", None),
+    ("varlen_gqa_fp32q_fp16kv_small", [300, 64, 1, 0, 517, 129], 32, 8, 0,
+     "fp32", "fp16", None),
+    ("outliers_1500tok_8q1kv", [1500], 8, 1, 0, "bf16", "bf16", None),
+]
+
+
+@pytest.mark.parametrize("case", FULL, ids=[c[0] for c in FULL])
+def test_full_parity(case):
+    name, lengths, hq, hkv, window, qd, kvd, scale = case
+    if lengths is None:
+        w = workloads.WORKLOADS[name]
+    else:
+        w = workloads.custom(name, lengths, hq, hkv, window=window, q_dtype=qd,
+                             kv_dtype=kvd, seed=21,
+                             k_outlier_frac=0.01 if "outliers" in name else 0.0,
+                             scale=scale)
+    _announce(f"{name} lengths={w.lengths or w.random_lengths} hq={w.n_q_heads} "
+              f"hkv={w.n_kv_heads} W={w.window} q={w.q_dtype} kv={w.kv_dtype}")
+    inp = workloads.make_inputs(w)
+    out = run_gpu(inp, w.n_q_heads, w.n_kv_heads, w.head_dim, w.attn_scale, w.window)
+    want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                   w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window)
+    check(name, to64(out), want)
+
+
+# ---------------------------------------------- small-shape grid (packed)
+GRID_LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 257, 0, 1, 200]
+GRID_WINDOWS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 256, 257, 258]
+GRID_HEADS = [(1, 1), (4, 1), (32, 1), (8, 8), (32, 8)]
+GRID_SCALES = [1 / math.sqrt(128), 0.0, 1.0, -0.3]
+
+
+@pytest.mark.parametrize("hq,hkv", GRID_HEADS)
+@pytest.mark.parametrize("scale", GRID_SCALES)
+def test_grid_windows_packed(hq, hkv, scale):
+    """All windows over one packed batch of ragged lengths per launch."""
+    w = workloads.custom("grid", GRID_LENGTHS, hq, hkv, seed=5 + hq + hkv)
+    inp = workloads.make_inputs(w)
+    for window in GRID_WINDOWS:
+        name = f"grid_h{hq}x{hkv}_s{scale:.3f}_w{window}"
+        _announce(name)
+        out = run_gpu(inp, hq, hkv, 128, scale, window)
+        want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"],
+                                       inp["cu_seqlens"], hq, hkv, scale, window)
+        check(name, to64(out), want)
+
+
+@pytest.mark.parametrize("qd,kvd", [("bf16", "fp16"), ("fp32", "bf16"), ("fp32", "fp16")])
+def test_dtype_variants(qd, kvd):
+    w = workloads.custom(f"dt_{qd}_{kvd}", [190, 33, 260], 8, 2, q_dtype=qd,
+                         kv_dtype=kvd, seed=31)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    for window in (0, 70):
+        out = run_gpu(inp, 8, 2, 128, w.attn_scale, window)
+        want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"],
+                                       inp["cu_seqlens"], 8, 2, w.attn_scale, window)
+        check(f"{w.name}_w{window}", to64(out), want)
+
+
+def test_window_one_returns_v_exactly_rounded():
+    """W = 1: every query sees only itself, so out = bf16(v) exactly."""
+    w = workloads.custom("w1", [300, 5], 4, 2, seed=41)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    out = run_gpu(inp, 4, 2, 128, w.attn_scale, 1).cpu()
+    for h in range(4):
+        assert torch.equal(out[:, h, :], inp["v"][:, h // 2, :])
+
+
+def test_first_token_of_each_sequence_is_its_v():
+    w = workloads.custom("first", [1, 130, 1, 64, 257], 4, 1, seed=42)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    out = run_gpu(inp, 4, 1, 128, w.attn_scale, 0).cpu()
+    cu = inp["cu_seqlens"].tolist()
+    for s in range(len(cu) - 1):
+        for h in range(4):
+            assert torch.equal(out[cu[s], h], inp["v"][cu[s], 0])
+
+
+# ------------------------------------------------- layouts and memory safety
+def test_strided_inputs_with_nan_gaps_and_output_canaries():
+    """Q/K/V are views into larger buffers whose gaps hold NaN; out is a view
+    into a buffer whose gaps hold a canary.  Any read across a head or token
+    boundary turns the output into NaN; any stray write breaks a canary."""
+    dev = torch.device("cuda:0")
+    lengths, hq, hkv, d = [150, 77, 200], 8, 2, 128
+    w = workloads.custom("strided", lengths, hq, hkv, seed=51)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    T = sum(lengths)
+
+    def padded(x, heads, pad_head, pad_tok, fill):
+        buf = torch.full((T + 2, heads * (d + pad_head) + pad_tok), fill,
+                         dtype=x.dtype)
+        view = buf[1:T + 1, :heads * (d + pad_head)].view(T, heads, d + pad_head)[:, :, :d]
+        view.copy_(x)
+        return buf.to(dev), (1, pad_head, pad_tok)
+
+    qb, _ = padded(inp["q"], hq, 8, 16, float("nan"))
+    kb, _ = padded(inp["k"], hkv, 64, 8, float("nan"))
+    vb, _ = padded(inp["v"], hkv, 16, 24, float("nan"))
+
+    def view_of(buf, heads, pad_head):
+        return buf[1:T + 1, :heads * (d + pad_head)].view(T, heads, d + pad_head)[:, :, :d]
+
+    q = view_of(qb, hq, 8)
+    k = view_of(kb, hkv, 64)
+    v = view_of(vb, hkv, 16)
+    canary = -12352.0  # exactly representable in bf16
+    ob = torch.full((T + 2, hq * (d + 8) + 8), canary, dtype=torch.bfloat16, device=dev)
+    out = view_of(ob, hq, 8)
+    binding.attn_prefill(q, k, v, out, inp["cu_seqlens"].to(dev), hq, hkv, d,
+                         w.attn_scale, 0)
+    torch.cuda.synchronize()
+    want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                   hq, hkv, w.attn_scale, 0)
+    check("strided_nan_gaps", to64(out), want)
+    mask = torch.ones_like(ob, dtype=torch.bool)
+    mask[1:T + 1, :hq * (d + 8)].view(T, hq, d + 8)[:, :, :d] = False
+    assert torch.all(ob[mask].float() == canary), "write outside the output view"
+
+
+def test_head_major_layout():
+    dev = torch.device("cuda:0")
+    w = workloads.custom("headmajor", [140, 260], 4, 1, seed=52)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    T = sum(w.lengths)
+    q = inp["q"].permute(1, 0, 2).contiguous().to(dev).permute(1, 0, 2)  # [H,T,d] storage
+    k = inp["k"].permute(1, 0, 2).contiguous().to(dev).permute(1, 0, 2)
+    v = inp["v"].to(dev)
+    out = torch.empty(4, T, 128, dtype=torch.bfloat16, device=dev).permute(1, 0, 2)
+    binding.attn_prefill(q, k, v, out, inp["cu_seqlens"].to(dev), 4, 1, 128,
+                         w.attn_scale, 0)
+    torch.cuda.synchronize()
+    want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                   4, 1, w.attn_scale, 0)
+    check("head_major", to64(out), want)
+
+
+def test_deterministic_bitwise():
+    w = workloads.custom("det", [700, 300], 32, 1, seed=53)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    a = run_gpu(inp, 32, 1, 128, w.attn_scale, 0).clone()
+    b = run_gpu(inp, 32, 1, 128, w.attn_scale, 0)
+    assert torch.equal(a, b)
+
+
+def test_malformed_offsets_stay_in_bounds():
+    """Offsets past T, decreasing or negative are clamped in the kernel: the
+    call completes and nothing outside `out` is written."""
+    dev = torch.device("cuda:0")
+    T, hq, d = 300, 4, 128
+    w = workloads.custom("malformed", [T], hq, 1, seed=54)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    ob = torch.full((T + 4, hq, d), 7.0, dtype=torch.bfloat16, device=dev)
+    out = ob[2:T + 2]
+    for cu in ([0, 5000], [0, 200, 100, 300], [-50, 120, 99999], [0, 300, 0, 300]):
+        cu_t = torch.tensor(cu, dtype=torch.int32, device=dev)
+        binding.attn_prefill(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+                             out, cu_t, hq, 1, d, w.attn_scale, 0)
+        torch.cuda.synchronize()
+        assert torch.all(ob[:2].float() == 7.0) and torch.all(ob[T + 2:].float() == 7.0)
+        assert torch.all(torch.isfinite(out[:120].float()))
+    # well-formed offsets on the same buffers still give the right answer
+    cu_t = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    binding.attn_prefill(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev), out,
+                         cu_t, hq, 1, d, w.attn_scale, 0)
+    torch.cuda.synchronize()
+    want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                   hq, 1, w.attn_scale, 0)
+    check("after_malformed", to64(out), want)
+
+
+def test_validate_env_rejects_bad_offsets(monkeypatch):
+    dev = torch.device("cuda:0")
+    w = workloads.custom("validate", [64], 1, 1, seed=55)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    monkeypatch.setenv("ATTN_PREFILL_VALIDATE", "1")
+    out = torch.empty(64, 1, 128, dtype=torch.bfloat16, device=dev)
+    bad = torch.tensor([0, 65], dtype=torch.int32, device=dev)
+    with pytest.raises(binding.AttnPrefillError) as e:
+        binding.attn_prefill(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+                             out, bad, 1, 1, 128, w.attn_scale, 0)
+    assert e.value.status == binding.ATTN_ERR_INVALID_ARG
+
+
+def test_native_library_is_loaded():
+    w = workloads.custom("native", [16], 1, 1, seed=56)
+    run_gpu(workloads.make_inputs(w), 1, 1, 128, w.attn_scale, 0)
+    maps = open("/proc/self/maps").read()
+    assert os.path.realpath(binding.LIB_PATH) in maps
+
+
+# ---------------------------------------- full-size workloads, sampled rows
+@pytest.mark.parametrize("name", [n for n in workloads.WORKLOADS])
+def test_full_size_sampled(name):
+    w = workloads.WORKLOADS[name]
+    _announce(f"full-size {name}")
+    inp = workloads.make_inputs(w)
+    out = run_gpu(inp, w.n_q_heads, w.n_kv_heads, w.head_dim, w.attn_scale, w.window)
+    rows = workloads.sample_rows(inp["lengths"], w.n_q_heads, 256, seed=w.seed)
+    want = oracle.attention_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                 w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window,
+                                 rows)
+    got = to64(out)
+    got_rows = np.stack([got[t, h] for t, h in rows])
+    check(f"{name}_sampled{len(rows)}", got_rows, want)
+    assert np.all(np.isfinite(got)), "non-finite output somewhere"
