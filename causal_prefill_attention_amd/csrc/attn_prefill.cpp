@@ -164,7 +164,7 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
       overlaps(eo, extent_of(v, n_kv_heads, head_dim)))
     return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
 
-  const int bm = attnp::prefill_block_m(head_dim);
+  const int bm = attnp::prefill_min_block_m(head_dim);
   const int64_t slots = (T + bm - 1) / bm + cu_seqlens->n_seqs;
   const int64_t blocks = slots * n_q_heads;
   if (slots > INT32_MAX || blocks * 256 >= ((int64_t)1 << 32))
@@ -195,7 +195,7 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
   p.n_q_heads = n_q_heads;
   p.group = n_q_heads / n_kv_heads;
   p.window = sliding_window;
-  p.tile_slots = (int32_t)slots;
+  p.tile_slots = 0;  // set by the launcher
   const float log2e = 1.4426950408889634f;
   if (scale == 0.f) {
     p.score_mult = 1.f;  // Q is zeroed, every visible score is 0

@@ -10,18 +10,31 @@
 //   log2(e) folded into the score multiplier.
 //
 // Design (ours, for CDNA4 -- the pages' GB10 / M40 kernels are prior art):
+//   * 8 waves per workgroup, two per SIMD, 32 query rows per wave, 256 rows
+//     per workgroup, 64-key tiles.  The waves form two groups (A = waves 0-3,
+//     B = waves 4-7; wave w and w + 4 share a SIMD) that run in anti-phase:
+//     in each barrier-delimited slot one group issues its matrix work
+//     [P(j-1) V(j-1), then S(j) = K(j) Q^T] while the other runs the softmax
+//     of its previous tile on the vector ALU, so the SIMD's matrix core and
+//     vector ALU are fed by different waves.  K(j) and V(j-1) stay in LDS for
+//     both slots; group A stages the next tiles (global loads in its matrix
+//     slot, LDS stores in its softmax slot) into the other LDS buffers.
 //   * Both contractions use v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-//   * Scores are formed transposed, S^T = K Q^T (keys on the MFMA M axis,
-//     queries on N), so every lane owns ONE query column: the per-query max
+//     Scores are formed transposed, S^T = K Q^T (keys on the MFMA M axis,
+//     queries on N), so every lane owns one query column: the per-query max
 //     and sum reduce 16 values in-lane plus one lane-pair exchange
 //     (v_permlane32_swap), and the softmax row scale is one scalar per lane.
 //   * The S^T accumulator, rounded to bf16, is directly the B operand of
 //     O^T += V^T P^T.  The key order inside each 16-key MFMA step follows the
 //     accumulator layout; V^T is written into LDS in that permuted order.
-//   * K is staged row-major in LDS, V transposed (V^T), both padded so that
-//     the 16-byte operand reads are bank-conflict free; the next tile is
-//     fetched into registers while the current one is consumed (two LDS
-//     stages, one barrier per tile).
+//   * The running max moves lazily: O and l are rescaled only when a query's
+//     max grows by more than 2^kLazy (a rare wave-uniform branch); l sums the
+//     bf16-rounded probabilities with v_dot2 so it matches what P.V uses.
+//   * Masks are applied only to tiles that straddle the diagonal or the
+//     window edge; a wave skips tiles none of its rows can see.
+//   * K/V tiles are read with buffer loads whose range covers only the
+//     tile's valid rows: keys past the tile's last query or the sequence read
+//     as zero with no branch and no vector address arithmetic.
 //   * Varlen: the grid covers an upper bound of q-tile slots; each workgroup
 //     decodes its (sequence, tile) from cu_seqlens with a wave-wide scan, so
 //     the host never reads the offsets.  Each sequence's tiles run heaviest
@@ -48,10 +61,16 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;      // two groups of four, one wave of each per SIMD
 constexpr int kThreads = kWave * kWaves;
-constexpr int kBM = 128;  // query rows per workgroup: 32 per wave
-constexpr int kBN = 64;   // keys per KV tile: two 32-key MFMA blocks
+constexpr int kBN = 64;        // keys per KV tile: two 32-key MFMA blocks
+constexpr int kKB = kBN / 32;
+constexpr int kKT = kBN / 16;  // 16-key MFMA k-steps of the P.V contraction
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+// Lazy-max threshold (log2 units): p = 2^(t - m) may reach 2^kLazy before m moves.
+constexpr float kLazy = 8.0f;
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int HDIM>
 struct Cfg {
@@ -60,14 +79,15 @@ struct Cfg {
   static constexpr int VSTR = kBN + 8;   // V^T row pitch in LDS (bf16 elements)
   static constexpr int K_ELEMS = kBN * KSTR;
   static constexpr int V_ELEMS = HDIM * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
   static constexpr int DCH = HDIM / 16;   // MFMA k-steps of the Q.K contraction
   static constexpr int DBLK = HDIM / 32;  // 32-wide output column blocks
   static constexpr int OCTS = HDIM / 8;   // 16-byte chunks per row
-  static constexpr int K_CHUNKS = kBN * OCTS / kThreads;
-  static constexpr int V_UNITS = (kBN / 4) * OCTS / kThreads;  // 4 keys x 8 d
-  static_assert(K_CHUNKS * kThreads == kBN * OCTS, "K tile split");
-  static_assert(V_UNITS * kThreads == (kBN / 4) * OCTS, "V tile split");
+  // Group A (256 threads) stages every tile.
+  static constexpr int STAGERS = kThreads / 2;
+  static constexpr int K_CHUNKS = kBN * OCTS / STAGERS;  // 16-byte K chunks per thread
+  static constexpr int V_UNITS = (kBN / 4) * OCTS / STAGERS;  // 4-key x 8-d V units
+  static_assert(K_CHUNKS * STAGERS == kBN * OCTS, "K tile split");
+  static_assert(V_UNITS * STAGERS == (kBN / 4) * OCTS, "V tile split");
 };
 
 // ---------------------------------------------------------------- element io
@@ -138,6 +158,7 @@ struct Work {
 // Maps a q-tile slot to (sequence, tile).  Slots enumerate sequences in
 // order; inside a sequence the last (most expensive causal) tile comes
 // first.  Every lane of the wave computes the same answer.
+template <int BM>
 __device__ Work decode_work(const PrefillParams& p, int slot) {
   const int lane = threadIdx.x & (kWave - 1);
   int base = 0;
@@ -149,7 +170,7 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
       b = min(max(p.cu_seqlens[s + 1], 0), p.n_tokens);
     }
     const int len = max(b - a, 0);
-    const int nt = (len + kBM - 1) / kBM;
+    const int nt = (len + BM - 1) / BM;
     int incl = nt;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -166,7 +187,7 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
       w.len = __shfl(len, src, kWave);
       const int ntiles = __shfl(nt, src, kWave);
       const int rank = slot - base - excl;  // 0 = heaviest tile
-      w.q0 = (ntiles - 1 - rank) * kBM;
+      w.q0 = (ntiles - 1 - rank) * BM;
       w.valid = true;
       return w;
     }
@@ -178,35 +199,42 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
 
 // ------------------------------------------------------------------ kernel
 template <int HDIM, class QT, class KVT>
-__global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams p) {
   using C = Cfg<HDIM>;
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+  // K stages [2][kBN][KSTR] then V^T stages [2][HDIM][VSTR] (bf16 bits).
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::K_ELEMS + 2 * C::V_ELEMS];
+  uint16_t* const kstage0 = smem;
+  uint16_t* const vstage0 = smem + 2 * C::K_ELEMS;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const int group = wave >> 2;                                   // 0 = A, 1 = B
   const int slot = blockIdx.x / p.n_q_heads;
   const int head = blockIdx.x - slot * p.n_q_heads;
-  const Work w = decode_work(p, slot);
+  Work w = decode_work<kBM>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
+  w.start = __builtin_amdgcn_readfirstlane(w.start);
+  w.len = __builtin_amdgcn_readfirstlane(w.len);
+  w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
 
   const int kvh = head / p.group;
   const int q_end = min(w.len, w.q0 + kBM);
-  const int kv_hi = q_end;  // last query of the tile sees keys < q_end
+  const int kv_hi = q_end;  // the tile's last query sees keys < q_end
   const int kv_lo = p.window > 0 ? max(0, w.q0 - p.window + 1) : 0;
   const int kv_start = kv_lo - kv_lo % kBN;
   const int n_tiles = (kv_hi - kv_start + kBN - 1) / kBN;
 
-  const int col = lane & 31;   // query column of this lane inside the wave
+  const int col = lane & 31;   // query column of this lane
   const int half = lane >> 5;  // which 8-wide half of each 16-wide k-step
-  const int wq0 = w.q0 + wave * 32;
+  const int wq0 = w.q0 + wave * 32;  // first row of this wave
   const int wq_last = min(wq0 + 31, w.len - 1);
   const bool wave_live = wq0 < w.len;
   const int myq = wq0 + col;
 
-  // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7] for every c.
+  // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7].
   bf16x8_t qf[C::DCH];
   {
     const bool ok = myq < w.len;
@@ -228,56 +256,70 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(PrefillParams 
     }
   }
 
-  const kvelem* kbase = static_cast<const kvelem*>(p.k) + (int64_t)kvh * p.k_hs;
-  const kvelem* vbase = static_cast<const kvelem*>(p.v) + (int64_t)kvh * p.v_hs;
+  // ---- K/V tile movement (group A only).  Per-sequence bases are
+  // wave-uniform; each tile is read through a buffer resource covering only
+  // its valid rows.
+  const kvelem* kseq = static_cast<const kvelem*>(p.k) + (int64_t)w.start * p.k_ts +
+                       (int64_t)kvh * p.k_hs;
+  const kvelem* vseq = static_cast<const kvelem*>(p.v) + (int64_t)w.start * p.v_ts +
+                       (int64_t)kvh * p.v_hs;
+  const int k_row_bytes = (int)(p.k_ts * (int64_t)sizeof(kvelem));
+  const int v_row_bytes = (int)(p.v_ts * (int64_t)sizeof(kvelem));
 
   u32x4_t kst[C::K_CHUNKS];
   u32x4_t vst[C::V_UNITS][4];
 
-  // Global -> registers for the tile starting at local key kv0.  Keys at or
-  // past kv_hi (beyond the tile's last query, or the sequence) read as zero.
-  auto gload = [&](int kv0) {
+  auto rows_of = [&](int kv0) {
+    // (readfirstlane keeps the descriptor scalar: a VALU min/max here would
+    // force a waterfall loop around every buffer load)
+    return __builtin_amdgcn_readfirstlane(max(0, min(kv_hi - kv0, kBN)));
+  };
+  auto gload_k = [&](int kv0) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<kvelem*>(kseq + (int64_t)kv0 * p.k_ts), 0, rows_of(kv0) * k_row_bytes,
+        kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int chunk = tid + i * kThreads;
-      const int row = chunk / C::OCTS;
-      const int oct = chunk % C::OCTS;
-      const int key = kv0 + row;
-      kst[i] = (u32x4_t){0u, 0u, 0u, 0u};
-      if (key < kv_hi) kst[i] = load16(kbase + (int64_t)(w.start + key) * p.k_ts + 8 * oct);
-    }
-#pragma unroll
-    for (int u = 0; u < C::V_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int kq = unit & 15;
-      const int oct = unit >> 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kv0 + 4 * kq + i;
-        vst[u][i] = (u32x4_t){0u, 0u, 0u, 0u};
-        if (key < kv_hi) vst[u][i] = load16(vbase + (int64_t)(w.start + key) * p.v_ts + 8 * oct);
-      }
+      const int chunk = tid + i * C::STAGERS;
+      kst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          r, (chunk / C::OCTS) * k_row_bytes + 16 * (chunk % C::OCTS), 0, 0);
     }
   };
-
-  // Registers -> LDS stage.  K row-major; V transposed with the key order of
-  // the S^T accumulator: inside each 16-key group, LDS positions 4..7 hold
-  // keys 8..11 and positions 8..11 hold keys 4..7.
-  auto lds_store = [&](int stage) {
-    uint16_t* ks = smem + stage * C::STAGE;
-    uint16_t* vs = ks + C::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int chunk = tid + i * kThreads;
-      const int row = chunk / C::OCTS;
-      const int oct = chunk % C::OCTS;
-      *reinterpret_cast<u32x4_t*>(ks + row * C::KSTR + 8 * oct) = kv_to_bf16(KVT(), kst[i]);
-    }
+  auto gload_v = [&](int kv0) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<kvelem*>(vseq + (int64_t)kv0 * p.v_ts), 0, rows_of(kv0) * v_row_bytes,
+        kRsrcWord3);
 #pragma unroll
     for (int u = 0; u < C::V_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int kq = unit & 15;
-      const int oct = unit >> 4;
+      const int unit = tid + u * C::STAGERS;
+      const int kq = unit % (kBN / 4);
+      const int oct = unit / (kBN / 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vst[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            r, (4 * kq + i) * v_row_bytes + 16 * oct, 0, 0);
+    }
+  };
+  // K row-major into stage `st`.
+  auto store_k = [&](int st) {
+    uint16_t* ks = kstage0 + st * C::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < C::K_CHUNKS; ++i) {
+      const int chunk = tid + i * C::STAGERS;
+      *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
+          kv_to_bf16(KVT(), kst[i]);
+    }
+  };
+  // V transposed into stage `st` with the key order of the S^T accumulator:
+  // inside each 16-key group, LDS positions 4..7 hold keys 8..11 and
+  // positions 8..11 hold keys 4..7.
+  auto store_v = [&](int st) {
+    uint16_t* vs = vstage0 + st * C::V_ELEMS;
+#pragma unroll
+    for (int u = 0; u < C::V_UNITS; ++u) {
+      const int unit = tid + u * C::STAGERS;
+      const int kq = unit % (kBN / 4);
+      const int oct = unit / (kBN / 4);
       const int qq = kq & 3;
       const int pos = 16 * (kq >> 2) + 4 * (((qq & 1) << 1) | (qq >> 1));
       u32x4_t r[4];
@@ -285,110 +327,159 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(PrefillParams 
       for (int i = 0; i < 4; ++i) r[i] = kv_to_bf16(KVT(), vst[u][i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int dw = j >> 1;
+        // element j of keys (i, i+1) -> one dword (v_perm_b32)
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
         u32x2_t out;
-        if (j & 1) {
-          out[0] = (r[0][dw] >> 16) | (r[1][dw] & 0xffff0000u);
-          out[1] = (r[2][dw] >> 16) | (r[3][dw] & 0xffff0000u);
-        } else {
-          out[0] = (r[0][dw] & 0xffffu) | (r[1][dw] << 16);
-          out[1] = (r[2][dw] & 0xffffu) | (r[3][dw] << 16);
-        }
+        out[0] = __builtin_amdgcn_perm(r[1][j >> 1], r[0][j >> 1], sel);
+        out[1] = __builtin_amdgcn_perm(r[3][j >> 1], r[2][j >> 1], sel);
         *reinterpret_cast<u32x2_t*>(vs + (8 * oct + j) * C::VSTR + pos) = out;
       }
     }
   };
 
-  gload(kv_start);
-  lds_store(0);
-  __syncthreads();
-
+  // ---- per-wave state
   f32x16_t o[C::DBLK];
 #pragma unroll
   for (int c = 0; c < C::DBLK; ++c) o[c] = (f32x16_t){};
-  float m_run = -INFINITY;  // running max of raw scores q.k
+  f32x16_t s[kKB];
+  bf16x8_t pf[kKT];
+  float m_run = -INFINITY;  // running (lazy) max of raw scores
   float l_run = 0.f;        // this lane's share of the running sum
   const float cmul = p.score_mult;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int kv0 = kv_start + it * kBN;
-    const bool more = it + 1 < n_tiles;
-    if (more) gload(kv0 + kBN);
-    const uint16_t* ks = smem + (it & 1) * C::STAGE;
-    const uint16_t* vs = ks + C::K_ELEMS;
+  // Whether any key of the tile at kv0 is visible to some row of this wave,
+  // and whether every key is visible to every row.
+  auto tile_seen = [&](int kv0) {
+    return wave_live && kv0 <= wq_last &&
+           (p.window == 0 || kv0 + kBN - 1 >= wq0 - p.window + 1);
+  };
+  auto tile_full = [&](int kv0) {
+    return (kv0 + kBN - 1 <= wq0) && (p.window == 0 || kv0 >= wq_last - p.window + 1);
+  };
 
-    const bool skip = !wave_live || kv0 > wq_last ||
-                      (p.window > 0 && kv0 + kBN - 1 < wq0 - p.window + 1);
-    if (!skip) {
-      // ---- S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks).
-      f32x16_t s[2] = {(f32x16_t){}, (f32x16_t){}};
+  // S^T = K Q^T for the tile in K stage `st`.
+  auto scores = [&](int st) {
+    const uint16_t* ks = kstage0 + st * C::K_ELEMS;
 #pragma unroll
-      for (int c = 0; c < C::DCH; ++c) {
+    for (int kb = 0; kb < kKB; ++kb) s[kb] = (f32x16_t){};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              ks + (32 * kb + col) * C::KSTR + 16 * c + 8 * half);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
-        }
+    for (int c = 0; c < C::DCH; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            ks + (32 * kb + col) * C::KSTR + 16 * c + 8 * half);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
-      // ---- mask (only tiles that straddle the diagonal or the window edge)
-      const bool full = (kv0 + kBN - 1 <= wq0) &&
-                        (p.window == 0 || kv0 >= wq_last - p.window + 1);
-      if (!full) {
+    }
+  };
+  // O^T += V^T P^T for the tile in V stage `st`.
+  auto pv = [&](int st) {
+    const uint16_t* vs = vstage0 + st * C::V_ELEMS;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+    for (int c = 0; c < C::DBLK; ++c) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = key <= myq && (p.window == 0 || key > myq - p.window);
-            if (!vis) s[kb][r] = -INFINITY;
-          }
-        }
+      for (int kt = 0; kt < kKT; ++kt) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            vs + (32 * c + col) * C::VSTR + 16 * kt + 8 * half);
+        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
       }
-      // ---- online softmax (base 2): running max m, sum l, rescale O.
-      float mx = -INFINITY;
+    }
+  };
+  // Mask (boundary tiles only), online softmax into the bf16 P operand, and
+  // the lazy rescale of O and l.
+  auto softmax = [&](int kv0) {
+    if (!tile_full(kv0)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      }
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * cmul);
-      const float neg_mc = -m_use * cmul;
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < C::DBLK; ++c) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-      }
-      bf16x8_t pf[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        u32x4_t u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e], cmul, neg_mc));
-          const float p1 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e + 1], cmul, neg_mc));
-          l_run += p0 + p1;
-          u[e] = pack_bf16x2(p0, p1);
-        }
-        pf[kt] = __builtin_bit_cast(bf16x8_t, u);
-      }
-      m_run = m_new;
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int c = 0; c < C::DBLK; ++c) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              vs + (32 * c + col) * C::VSTR + 16 * kt + 8 * half);
-          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key <= myq && (p.window == 0 || key > myq - p.window);
+          if (!vis) s[kb][r] = -INFINITY;
         }
       }
     }
-    if (more) lds_store((it + 1) & 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair_max(mx);
+    const bool raise = (mx - m_run) * cmul > kLazy;  // true when m_run = -inf < mx
+    const bool any = __ballot(raise) != 0ull;        // wave-uniform
+    const float m_new = any ? fmaxf(m_run, mx) : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
+    const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
+    m_run = m_new;
+    float l = l_run * alpha;
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt) {
+      u32x4_t u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e], cmul, neg_mc));
+        const float p1 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e + 1], cmul, neg_mc));
+        // The dot product takes the converted pair itself: bit-casting an
+        // element of `u` back to bf16x2 made hipcc (ROCm 7.2) feed the same
+        // register to every v_dot2c of the group.
+        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        u[e] = __builtin_bit_cast(uint32_t, pb);
+        // l accumulates the bf16-rounded p that the P.V product uses
+        l = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l, false);
+      }
+      pf[kt] = __builtin_bit_cast(bf16x8_t, u);
+    }
+    l_run = l;
+    if (any) {
+#pragma unroll
+      for (int c = 0; c < C::DBLK; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
+    }
+  };
+
+  // ---- prologue: K(0) in stage 0.
+  if (group == 0) {
+    gload_k(kv_start);
+    store_k(0);
+  }
+  __syncthreads();
+
+  // ---- ping-pong slots.  Each barrier ends a slot.  In slot 2j group A
+  // runs its matrix work for tile j (P(j-1)V(j-1), then S(j)) while group B
+  // runs softmax(j-1); in slot 2j+1 group A runs softmax(j) while group B
+  // runs its matrix work for tile j.  Tile j uses K stage j&1 and V stage
+  // j&1.  Group A loads K(j+1), V(j) during its matrix slot of tile j and
+  // stores them during its softmax slot, into the stages that nobody reads in
+  // those two slots.  Both groups pass the same 2n + 2 barriers.
+  if (group == 0) {
+    for (int j = 0; j < n_tiles; ++j) {
+      const int kv0 = kv_start + j * kBN;
+      if (j >= 1 && tile_seen(kv0 - kBN)) pv((j - 1) & 1);
+      if (tile_seen(kv0)) scores(j & 1);
+      if (j + 1 < n_tiles) gload_k(kv0 + kBN);
+      gload_v(kv0);
+      __syncthreads();
+      if (tile_seen(kv0)) softmax(kv0);
+      if (j + 1 < n_tiles) store_k((j + 1) & 1);
+      store_v(j & 1);
+      __syncthreads();
+    }
+    if (tile_seen(kv_start + (n_tiles - 1) * kBN)) pv((n_tiles - 1) & 1);
+    __syncthreads();
+    __syncthreads();
+  } else {
+    __syncthreads();
+    for (int j = 0; j < n_tiles; ++j) {
+      const int kv0 = kv_start + j * kBN;
+      if (j >= 1 && tile_seen(kv0 - kBN)) pv((j - 1) & 1);
+      if (tile_seen(kv0)) scores(j & 1);
+      __syncthreads();
+      if (tile_seen(kv0)) softmax(kv0);
+      __syncthreads();
+    }
+    if (tile_seen(kv_start + (n_tiles - 1) * kBN)) pv((n_tiles - 1) & 1);
     __syncthreads();
   }
 
@@ -413,8 +504,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fwd_kernel(PrefillParams 
 }
 
 template <int HDIM, class QT, class KVT>
-hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  const uint64_t blocks = (uint64_t)p.tile_slots * (uint64_t)p.n_q_heads;
+hipError_t launch_one(PrefillParams p, hipStream_t stream) {
+  const int64_t slots = (p.n_tokens + kBM - 1) / kBM + p.n_seqs;
+  p.tile_slots = (int32_t)slots;
+  const uint64_t blocks = (uint64_t)slots * (uint64_t)p.n_q_heads;
   hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT>), dim3((uint32_t)blocks),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
@@ -422,7 +515,7 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int prefill_block_m(int /*head_dim*/) { return kBM; }
+int prefill_min_block_m(int /*head_dim*/) { return kBM; }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
                           DType kv_dtype, hipStream_t stream) {

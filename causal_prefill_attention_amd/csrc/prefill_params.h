@@ -26,16 +26,18 @@ struct PrefillParams {
   int32_t n_q_heads;
   int32_t group;              // n_q_heads / n_kv_heads
   int32_t window;             // 0 = off
-  int32_t tile_slots;         // q-tile slots in the grid (>= real tiles)
+  int32_t tile_slots;         // q-tile slots in the grid (set by the launcher)
   float score_mult;           // log2(e) * |scale|, or 1 when scale == 0
   float q_mult;               // +1, -1 or 0: sign of scale folded into Q
 };
 
-// Rows of queries per workgroup for a head size (the grid is sized with it).
-int prefill_block_m(int head_dim);
+// Smallest number of query rows per workgroup any launch uses (the grid has
+// at most ceil(T / this) + n_seqs tile slots per query head).
+int prefill_min_block_m(int head_dim);
 
-// Launches the kernel for (head_dim, q dtype, kv dtype) on `stream`.
-// Returns hipErrorInvalidValue if no instantiation exists.
+// Launches the kernel for (head_dim, q dtype, kv dtype) on `stream`; picks
+// the workgroup size and sets p.tile_slots.  Returns hipErrorInvalidValue if
+// no instantiation exists.
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
                           DType kv_dtype, hipStream_t stream);
 
