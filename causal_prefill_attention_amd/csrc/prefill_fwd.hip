@@ -82,7 +82,7 @@ struct Cfg {
   static constexpr int DCH = HDIM / 16;   // MFMA k-steps of the Q.K contraction
   static constexpr int DBLK = HDIM / 32;  // 32-wide output column blocks
   static constexpr int OCTS = HDIM / 8;   // 16-byte chunks per row
-  // Group A (256 threads) stages every tile.
+  // Group A's 256 threads stage K, group B's stage V.
   static constexpr int STAGERS = kThreads / 2;
   static constexpr int K_CHUNKS = kBN * OCTS / STAGERS;  // 16-byte K chunks per thread
   static constexpr int V_UNITS = (kBN / 4) * OCTS / STAGERS;  // 4-key x 8-d V units
@@ -256,9 +256,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     }
   }
 
-  // ---- K/V tile movement (group A only).  Per-sequence bases are
-  // wave-uniform; each tile is read through a buffer resource covering only
-  // its valid rows.
+  // ---- K/V tile movement (K by group A, V by group B).  Per-sequence bases
+  // are wave-uniform; each tile is read through a buffer resource covering
+  // only its valid rows.
   const kvelem* kseq = static_cast<const kvelem*>(p.k) + (int64_t)w.start * p.k_ts +
                        (int64_t)kvh * p.k_hs;
   const kvelem* vseq = static_cast<const kvelem*>(p.v) + (int64_t)w.start * p.v_ts +
@@ -266,6 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int k_row_bytes = (int)(p.k_ts * (int64_t)sizeof(kvelem));
   const int v_row_bytes = (int)(p.v_ts * (int64_t)sizeof(kvelem));
 
+  const int stid = tid & (C::STAGERS - 1);  // index inside the staging group
   u32x4_t kst[C::K_CHUNKS];
   u32x4_t vst[C::V_UNITS][4];
 
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
         kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int chunk = tid + i * C::STAGERS;
+      const int chunk = stid + i * C::STAGERS;
       kst[i] = __builtin_amdgcn_raw_buffer_load_b128(
           r, (chunk / C::OCTS) * k_row_bytes + 16 * (chunk % C::OCTS), 0, 0);
     }
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
         kRsrcWord3);
 #pragma unroll
     for (int u = 0; u < C::V_UNITS; ++u) {
-      const int unit = tid + u * C::STAGERS;
+      const int unit = stid + u * C::STAGERS;
       const int kq = unit % (kBN / 4);
       const int oct = unit / (kBN / 4);
 #pragma unroll
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     uint16_t* ks = kstage0 + st * C::K_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int chunk = tid + i * C::STAGERS;
+      const int chunk = stid + i * C::STAGERS;
       *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
           kv_to_bf16(KVT(), kst[i]);
     }
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     uint16_t* vs = vstage0 + st * C::V_ELEMS;
 #pragma unroll
     for (int u = 0; u < C::V_UNITS; ++u) {
-      const int unit = tid + u * C::STAGERS;
+      const int unit = stid + u * C::STAGERS;
       const int kq = unit % (kBN / 4);
       const int oct = unit / (kBN / 4);
       const int qq = kq & 3;
@@ -348,12 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const float cmul = p.score_mult;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Whether any key of the tile at kv0 is visible to some row of this wave,
-  // and whether every key is visible to every row.
-  auto tile_seen = [&](int kv0) {
-    return wave_live && kv0 <= wq_last &&
-           (p.window == 0 || kv0 + kBN - 1 >= wq0 - p.window + 1);
-  };
+  // Whether every key of the tile at kv0 is visible to every row of this wave.
   auto tile_full = [&](int kv0) {
     return (kv0 + kBN - 1 <= wq0) && (p.window == 0 || kv0 >= wq_last - p.window + 1);
   };
@@ -386,6 +382,53 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
       }
     }
   };
+  // Matrix slot of tile j when both P(j-1)V(j-1) and S(j) are needed, as one
+  // straight-line block: the 16 P.V MFMAs (four accumulator chains), then
+  // the 16 score MFMAs, with every LDS operand read kAhead MFMAs ahead
+  // (across the boundary between the two products, too).
+  auto matrix_fused = [&](int kst_i, int vst_i) {
+    const uint16_t* ks = kstage0 + kst_i * C::K_ELEMS;
+    const uint16_t* vs = vstage0 + vst_i * C::V_ELEMS;
+    static_assert(C::DBLK * kKT == 16 && C::DCH * kKB == 16, "32-MFMA matrix slot");
+    // operand i < 16: V^T for P.V step i (kt-major over the 4 output blocks);
+    // i >= 16: K for score step i - 16 (d-chunk-major over the 2 key blocks)
+    auto operand = [&](int i) -> bf16x8_t {
+      if (i >= 16) {
+        const int c = (i - 16) >> 1, kb = i & 1;
+        return *reinterpret_cast<const bf16x8_t*>(ks + (32 * kb + col) * C::KSTR + 16 * c +
+                                                  8 * half);
+      }
+      const int kt = i >> 2, c = i & 3;
+      return *reinterpret_cast<const bf16x8_t*>(vs + (32 * c + col) * C::VSTR + 16 * kt +
+                                                8 * half);
+    };
+    constexpr int kAhead = 8;
+    bf16x8_t buf[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) buf[i] = operand(i);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const bf16x8_t a = buf[i % kAhead];
+      if (i + kAhead < 32) buf[i % kAhead] = operand(i + kAhead);
+      if (i >= 16) {
+        const int c = (i - 16) >> 1, kb = i & 1;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? (f32x16_t){} : s[kb],
+                                                        0, 0, 0);
+      } else {
+        const int kt = i >> 2, c = i & 3;
+        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
+      }
+    }
+    // pin the order: kAhead LDS reads, then (MFMA, LDS read) pairs, then the
+    // last kAhead MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < 32 - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+  };
   // Mask (boundary tiles only), online softmax into the bf16 P operand, and
   // the lazy rescale of O and l.
   auto softmax = [&](int kv0) {
@@ -400,11 +443,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
         }
       }
     }
-    float mx = -INFINITY;
+    // Row max and row sum use four independent partial chains each: with one
+    // vector-ALU wave per SIMD in this slot, a single 32-long dependency
+    // chain would leave the ALU waiting on latency.
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     mx = pair_max(mx);
     const bool raise = (mx - m_run) * cmul > kLazy;  // true when m_run = -inf < mx
     const bool any = __ballot(raise) != 0ull;        // wave-uniform
@@ -412,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
     const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
     m_run = m_new;
-    float l = l_run * alpha;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
       u32x4_t u;
@@ -426,11 +473,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
         const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
         u[e] = __builtin_bit_cast(uint32_t, pb);
         // l accumulates the bf16-rounded p that the P.V product uses
-        l = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l, false);
+        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
       }
       pf[kt] = __builtin_bit_cast(bf16x8_t, u);
     }
-    l_run = l;
+    l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
     if (any) {
 #pragma unroll
       for (int c = 0; c < C::DBLK; ++c)
@@ -439,10 +486,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     }
   };
 
-  // ---- prologue: K(0) in stage 0.
+  // ---- prologue: K(0) stored in stage 0 and K(1) in flight (group A),
+  // V(0) in flight (group B).
   if (group == 0) {
     gload_k(kv_start);
     store_k(0);
+    if (n_tiles > 1) gload_k(kv_start + kBN);
+  } else {
+    gload_v(kv_start);
   }
   __syncthreads();
 
@@ -450,36 +501,57 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   // runs its matrix work for tile j (P(j-1)V(j-1), then S(j)) while group B
   // runs softmax(j-1); in slot 2j+1 group A runs softmax(j) while group B
   // runs its matrix work for tile j.  Tile j uses K stage j&1 and V stage
-  // j&1.  Group A loads K(j+1), V(j) during its matrix slot of tile j and
-  // stores them during its softmax slot, into the stages that nobody reads in
-  // those two slots.  Both groups pass the same 2n + 2 barriers.
+  // j&1, both resident through slots 2j and 2j+1 and free during slots
+  // 2j-2 and 2j-1, when they are written.  Group A stages K and group B
+  // stages V, each at the end of its slot 2j-1 (A: softmax slot, B: matrix
+  // slot, after its MFMAs are issued): store the tile loaded two slots
+  // earlier, then issue the loads of the next one, so every load has two
+  // slots to arrive.  Both groups pass the same 2n + 2 barriers after the
+  // prologue.  Every wave runs every tile: a tile none of its rows can see
+  // is fully masked and contributes exact zeros.
   if (group == 0) {
-    for (int j = 0; j < n_tiles; ++j) {
+    // prologue (before the loop): K(0) stored, K(1) in flight
+    scores(0);
+    __syncthreads();
+    softmax(kv_start);
+    if (n_tiles > 1) {
+      store_k(1);
+      if (n_tiles > 2) gload_k(kv_start + 2 * kBN);
+    }
+    __syncthreads();
+    for (int j = 1; j < n_tiles; ++j) {
       const int kv0 = kv_start + j * kBN;
-      if (j >= 1 && tile_seen(kv0 - kBN)) pv((j - 1) & 1);
-      if (tile_seen(kv0)) scores(j & 1);
-      if (j + 1 < n_tiles) gload_k(kv0 + kBN);
-      gload_v(kv0);
+      matrix_fused(j & 1, (j - 1) & 1);
       __syncthreads();
-      if (tile_seen(kv0)) softmax(kv0);
-      if (j + 1 < n_tiles) store_k((j + 1) & 1);
-      store_v(j & 1);
+      softmax(kv0);
+      if (j + 1 < n_tiles) {
+        store_k((j + 1) & 1);
+        if (j + 2 < n_tiles) gload_k(kv0 + 2 * kBN);
+      }
       __syncthreads();
     }
-    if (tile_seen(kv_start + (n_tiles - 1) * kBN)) pv((n_tiles - 1) & 1);
+    pv((n_tiles - 1) & 1);
     __syncthreads();
     __syncthreads();
   } else {
     __syncthreads();
-    for (int j = 0; j < n_tiles; ++j) {
+    // V(0) was loaded before the first barrier
+    scores(0);
+    store_v(0);
+    if (n_tiles > 1) gload_v(kv_start + kBN);
+    __syncthreads();
+    softmax(kv_start);
+    __syncthreads();
+    for (int j = 1; j < n_tiles; ++j) {
       const int kv0 = kv_start + j * kBN;
-      if (j >= 1 && tile_seen(kv0 - kBN)) pv((j - 1) & 1);
-      if (tile_seen(kv0)) scores(j & 1);
+      matrix_fused(j & 1, (j - 1) & 1);
+      store_v(j & 1);
+      if (j + 1 < n_tiles) gload_v(kv0 + kBN);
       __syncthreads();
-      if (tile_seen(kv0)) softmax(kv0);
+      softmax(kv0);
       __syncthreads();
     }
-    if (tile_seen(kv_start + (n_tiles - 1) * kBN)) pv((n_tiles - 1) & 1);
+    pv((n_tiles - 1) & 1);
     __syncthreads();
   }
 
