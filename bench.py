@@ -129,7 +129,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="query heads of the workload the CPU oracle times "
-                         "(default: one per host thread)")
+                         "(default: all of them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["attn", "copy"], default="attn")
     ap.add_argument("--copy-mib", type=int, default=1024)
@@ -236,7 +236,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads or host_threads())
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads or w.n_q_heads)
     print(json.dumps(line), flush=True)
 
 

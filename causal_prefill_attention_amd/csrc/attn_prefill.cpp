@@ -157,6 +157,14 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
     return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens data is NULL");
   if (cu_seqlens->max_seqlen < 0)
     return fail(ATTN_ERR_INVALID_ARG, "max_seqlen %d < 0", (int)cu_seqlens->max_seqlen);
+  // K and V tiles are read through buffer resources with a 32-bit range and
+  // 32-bit offsets, one resource per tile of up to 64 rows.
+  for (const attn_tensor* t : {k, v}) {
+    if (T > 1 && t->token_stride * elem_bytes(t->dtype) * 64 > (int64_t)INT32_MAX)
+      return fail(ATTN_ERR_UNSUPPORTED,
+                  "%s: token stride of %lld bytes is too large (at most 32 MiB - 1 B)",
+                  t == k ? "k" : "v", (long long)(t->token_stride * elem_bytes(t->dtype)));
+  }
   if (T == 0) return ATTN_OK;  // nothing to compute or write
   const Extent eo = extent_of(out, n_q_heads, head_dim);
   if (overlaps(eo, extent_of(q, n_q_heads, head_dim)) ||
@@ -167,7 +175,7 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
   const int bm = attnp::prefill_min_block_m(head_dim);
   const int64_t slots = (T + bm - 1) / bm + cu_seqlens->n_seqs;
   const int64_t blocks = slots * n_q_heads;
-  if (slots > INT32_MAX || blocks * 256 >= ((int64_t)1 << 32))
+  if (slots > INT32_MAX || blocks * 1024 >= ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large",
                 (long long)blocks);
 

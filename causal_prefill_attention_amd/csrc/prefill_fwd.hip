@@ -31,7 +31,10 @@
 //     max grows by more than 2^kLazy (a rare wave-uniform branch); l sums the
 //     bf16-rounded probabilities with v_dot2 so it matches what P.V uses.
 //   * Masks are applied only to tiles that straddle the diagonal or the
-//     window edge; a wave skips tiles none of its rows can see.
+//     window edge.  Every wave runs every tile of its workgroup; a tile none
+//     of its rows can see is fully masked and adds exact zeros.
+//   * The epilogue stages each wave's normalised 32 x HDIM bf16 tile in its
+//     own LDS slice and stores whole rows, one 16-byte chunk per lane.
 //   * K/V tiles are read with buffer loads whose range covers only the
 //     tile's valid rows: keys past the tile's last query or the sequence read
 //     as zero with no branch and no vector address arithmetic.
@@ -555,22 +558,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     __syncthreads();
   }
 
-  // ---- epilogue: O / l -> bf16, rows of this sequence only.
+  // ---- epilogue: O / l -> bf16, rows of this sequence only.  The wave's
+  // 32 x HDIM tile goes through its own LDS slice (free after the last
+  // barrier) so that every global store writes whole 2*HDIM-byte rows.
   const float l_tot = pair_sum(l_run);
-  if (wave_live && myq < w.len) {
-    const float inv = 1.f / l_tot;
-    uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)(w.start + myq) * p.o_ts +
-                   (int64_t)head * p.o_hs;
+  if (wave_live) {
+    constexpr int OSTR = HDIM + 8;  // row pitch in LDS (bf16 elements)
+    static_assert(kWaves * 32 * OSTR <= 2 * C::K_ELEMS + 2 * C::V_ELEMS, "O slices fit");
+    uint16_t* ob = smem + wave * 32 * OSTR;
+    const float inv = 1.f / l_tot;  // rows past the sequence are never stored
 #pragma unroll
     for (int c = 0; c < C::DBLK; ++c) {
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const int d = 32 * c + 8 * rb + 4 * half;
         u32x2_t pk;
         pk[0] = pack_bf16x2(o[c][4 * rb] * inv, o[c][4 * rb + 1] * inv);
         pk[1] = pack_bf16x2(o[c][4 * rb + 2] * inv, o[c][4 * rb + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(op + d) = pk;
+        *reinterpret_cast<u32x2_t*>(ob + col * OSTR + 32 * c + 8 * rb + 4 * half) = pk;
       }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int CPR = HDIM / 8;          // 16-byte chunks per row
+    constexpr int RPI = kWave / CPR;       // rows per store instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + lane / CPR;
+      const int ch = lane % CPR;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ob + row * OSTR + 8 * ch);
+      if (wq0 + row < w.len)
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) +
+                                    (int64_t)(w.start + wq0 + row) * p.o_ts +
+                                    (int64_t)head * p.o_hs + 8 * ch) = v;
     }
   }
 }

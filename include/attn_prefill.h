@@ -80,7 +80,9 @@ typedef struct ihipStream_t* attn_stream_t;
  * the call's arguments).  Strides are in elements and must be >= 0; the
  * head vectors of different (token, head) pairs must not overlap.  data must
  * be 16-byte aligned and token_stride / head_stride must be multiples of
- * 16 bytes, else ATTN_ERR_UNSUPPORTED. */
+ * 16 bytes, else ATTN_ERR_UNSUPPORTED.  For k and v, 64 token strides must
+ * span less than 2 GiB (token_stride * element size < 32 MiB), else
+ * ATTN_ERR_UNSUPPORTED. */
 typedef struct {
   void* data;           /* device pointer, caller-owned; may be NULL if
                            n_tokens == 0                                   */

@@ -123,6 +123,11 @@ BAD = [
      B.ATTN_ERR_INVALID_ARG, "overlap head vectors"),
     ("misaligned_pointer", lambda a: with_(a, q=mutate(a["q"], data=FAKE + 2)),
      B.ATTN_ERR_UNSUPPORTED, "aligned"),
+    ("k_stride_beyond_buffer_range", lambda a: with_(a, k=mutate(a["k"], token_stride=1 << 24)),
+     B.ATTN_ERR_UNSUPPORTED, "k: token stride"),
+    ("v_stride_beyond_buffer_range",
+     lambda a: with_(a, v=mutate(a["v"], token_stride=(1 << 24) + 8)),
+     B.ATTN_ERR_UNSUPPORTED, "v: token stride"),
     ("stride_not_16_bytes", lambda a: with_(a, k=mutate(a["k"], token_stride=132)),
      B.ATTN_ERR_UNSUPPORTED, "16 bytes"),
     ("seqlens_null_data", lambda a: with_(a, seqlens=B.AttnSeqlens(None, 1, 0)),
