@@ -4,6 +4,7 @@ Imported by ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
 leg of ``bench.py``; never by the library or its binding.
 """
 from .attention import (  # noqa: F401
+    attention_chunked,
     attention_head,
     attention_rows,
     attention_varlen,

@@ -28,6 +28,16 @@ For each packed sequence ``s`` (tokens ``cu[s] .. cu[s+1]-1``, local indices
 5. ``O[s, h] = P @ V[s, g]``.
 6. Sequences never see each other.
 
+Chunked prefill against a KV history (``attention_chunked``): a later
+prefill chunk attends to every earlier token of its sequence, not only to
+the tokens of the chunk -- the multi-chunk fix on the atlas PR #69 page
+(later chunks use ``kv_len = seq_len_start + n``).  Sequence ``s`` then has
+``Lq`` new queries and ``Lk >= Lq`` keys/values (history followed by the
+chunk itself); query ``i`` sits at absolute position ``Lk - Lq + i`` and the
+visibility rule of step 3 is applied to that position.  With ``Lq == Lk``
+this is exactly the definition above.  A query with no visible key (only
+possible when ``Lq > Lk``, outside the contract) has an all-zero output row.
+
 The online-softmax recurrence that the GPU kernel uses (the fused MLA prefill
 commit on the atlas PR #69 page) is a reordering of steps 4-5 and is not
 used here.  The head grouping ``g = h // group`` is the consecutive GQA
@@ -48,6 +58,7 @@ __all__ = [
     "softmax_probs",
     "attention_head",
     "attention_varlen",
+    "attention_chunked",
     "attention_rows",
     "visible_pairs",
 ]
@@ -74,38 +85,53 @@ def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
     return h // group
 
 
-def visibility(n_rows: int, n_cols: int, window: int) -> np.ndarray:
-    """Boolean ``[n_rows, n_cols]``: may query ``i`` attend to key ``j``."""
-    i = np.arange(n_rows)[:, None]
+def visibility(n_rows: int, n_cols: int, window: int,
+               q_offset: int = 0) -> np.ndarray:
+    """Boolean ``[n_rows, n_cols]``: may query ``i`` attend to key ``j``.
+
+    Query ``i`` sits at absolute position ``q_offset + i`` (0 for a prefill
+    without history).
+    """
+    pos = q_offset + np.arange(n_rows)[:, None]
     j = np.arange(n_cols)[None, :]
-    vis = j <= i
+    vis = j <= pos
     if window > 0:
-        vis &= j >= i - window + 1
+        vis &= j >= pos - window + 1
     return vis
 
 
-def softmax_probs(q_h, k_g, scale: float, window: int) -> np.ndarray:
+def softmax_probs(q_h, k_g, scale: float, window: int,
+                  q_offset: Optional[int] = None) -> np.ndarray:
     """Attention probabilities ``P`` for one sequence and one head.
 
-    ``q_h``: ``[L, d]``, ``k_g``: ``[L, d]``.  Returns float64 ``[L, L]`` whose
-    rows sum to one over the visible keys and are exactly 0 elsewhere.
+    ``q_h``: ``[Lq, d]``, ``k_g``: ``[Lk, d]``; the queries are the last
+    ``Lq`` positions unless ``q_offset`` says otherwise.  Returns float64
+    ``[Lq, Lk]`` whose rows sum to one over the visible keys and are exactly
+    0 elsewhere (all 0 for a row without a visible key).
     """
     q_h = _as_f64(q_h)
     k_g = _as_f64(k_g)
-    n = q_h.shape[0]
+    n_q, n_k = q_h.shape[0], k_g.shape[0]
+    if q_offset is None:
+        q_offset = n_k - n_q
     s = float(scale) * (q_h @ k_g.T)
-    vis = visibility(n, n, window)
-    s = np.where(vis, s, -np.inf)
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    return e / e.sum(axis=1, keepdims=True)
+    vis = visibility(n_q, n_k, window, q_offset)
+    p = np.zeros((n_q, n_k), dtype=np.float64)
+    rows = vis.any(axis=1)
+    if rows.any():
+        sv = np.where(vis[rows], s[rows], -np.inf)
+        m = sv.max(axis=1, keepdims=True)
+        e = np.exp(sv - m)
+        p[rows] = e / e.sum(axis=1, keepdims=True)
+    return p
 
 
-def attention_head(q_h, k_g, v_g, scale: float, window: int) -> np.ndarray:
+def attention_head(q_h, k_g, v_g, scale: float, window: int,
+                   q_offset: Optional[int] = None) -> np.ndarray:
     """``O = softmax(scale * Q K^T + mask) V`` for one sequence, one head."""
     if np.shape(q_h)[0] == 0:
         return np.zeros((0, np.shape(v_g)[1]), dtype=np.float64)
-    p = softmax_probs(q_h, k_g, scale, window)
+    p = softmax_probs(q_h, k_g, scale, window, q_offset)
     return p @ _as_f64(v_g)
 
 
@@ -150,16 +176,65 @@ def attention_varlen(q, k, v, cu_seqlens, n_q_heads: int, n_kv_heads: int,
     return out
 
 
+def attention_chunked(q, k, v, cu_seqlens_q, cu_seqlens_k, n_q_heads: int,
+                      n_kv_heads: int, scale: float, window: int,
+                      workers: Optional[int] = None) -> np.ndarray:
+    """Chunked prefill against a KV history, float64 ``[Tq, n_q_heads, d_v]``.
+
+    ``q``: ``[Tq, n_q_heads, d]`` packed by ``cu_seqlens_q``; ``k``, ``v``:
+    ``[Tk, n_kv_heads, d]`` packed by ``cu_seqlens_k`` (same number of
+    sequences).  Sequence ``s``'s queries are the last ``Lq`` of its ``Lk``
+    positions.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    cq = _as_offsets(cu_seqlens_q)
+    ck = _as_offsets(cu_seqlens_k)
+    if len(cq) != len(ck):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+    if n_q_heads % n_kv_heads != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    out = np.zeros((q.shape[0], n_q_heads, v.shape[2]), dtype=np.float64)
+    jobs = [(s, h) for s in range(len(cq) - 1) for h in range(n_q_heads)
+            if cq[s + 1] > cq[s]]
+
+    def run(job):
+        s, h = job
+        a, b = cq[s], cq[s + 1]
+        ka, kb = ck[s], ck[s + 1]
+        g = kv_head_of(h, n_q_heads, n_kv_heads)
+        out[a:b, h, :] = attention_head(q[a:b, h, :], k[ka:kb, g, :],
+                                        v[ka:kb, g, :], scale, window,
+                                        (kb - ka) - (b - a))
+
+    n_workers = workers if workers is not None else (os.cpu_count() or 1)
+    if n_workers <= 1 or len(jobs) <= 1:
+        for job in jobs:
+            run(job)
+        return out
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        with concurrent.futures.ThreadPoolExecutor(n_workers) as pool:
+            for f in [pool.submit(run, job) for job in jobs]:
+                f.result()
+    return out
+
+
 def attention_rows(q, k, v, cu_seqlens, n_q_heads: int, n_kv_heads: int,
                    scale: float, window: int,
-                   rows: Iterable[Tuple[int, int]]) -> np.ndarray:
+                   rows: Iterable[Tuple[int, int]],
+                   cu_seqlens_k=None) -> np.ndarray:
     """The same definition evaluated one output row at a time.
 
     ``rows`` lists ``(token, q_head)`` pairs; returns float64
     ``[len(rows), d_v]``.  Used for spot checks at sizes where the full
-    result is too slow to form.
+    result is too slow to form.  With ``cu_seqlens_k`` the keys come from a
+    KV history as in ``attention_chunked``.
     """
     cu = _as_offsets(cu_seqlens)
+    ck = cu if cu_seqlens_k is None else _as_offsets(cu_seqlens_k)
     rows = list(rows)
     q_t = q
     res = np.zeros((len(rows), np.shape(v)[2]), dtype=np.float64)
@@ -167,22 +242,30 @@ def attention_rows(q, k, v, cu_seqlens, n_q_heads: int, n_kv_heads: int,
         s = int(np.searchsorted(np.asarray(cu), tok, side="right")) - 1
         while cu[s + 1] <= tok:  # skip empty sequences sharing the offset
             s += 1
-        a = cu[s]
-        i = tok - a
-        lo = 0 if window == 0 else max(0, i - window + 1)
+        pos = (ck[s + 1] - ck[s]) - (cu[s + 1] - cu[s]) + (tok - cu[s])
+        lo = 0 if window == 0 else max(0, pos - window + 1)
+        if pos < 0:
+            continue  # no visible key: zero row
         g = kv_head_of(h, n_q_heads, n_kv_heads)
         qi = _as_f64(q_t[tok, h, :])
-        kk = _as_f64(k[a + lo:a + i + 1, g, :])
-        vv = _as_f64(v[a + lo:a + i + 1, g, :])
+        kk = _as_f64(k[ck[s] + lo:ck[s] + pos + 1, g, :])
+        vv = _as_f64(v[ck[s] + lo:ck[s] + pos + 1, g, :])
         sc = float(scale) * (kk @ qi)
         e = np.exp(sc - sc.max())
         res[r] = (e / e.sum()) @ vv
     return res
 
 
-def visible_pairs(lengths: Sequence[int], window: int) -> int:
-    """Number of visible (query, key) pairs, summed over sequences."""
+def visible_pairs(lengths: Sequence[int], window: int,
+                  q_lengths: Optional[Sequence[int]] = None) -> int:
+    """Number of visible (query, key) pairs, summed over sequences.
+
+    ``lengths`` are the key counts; ``q_lengths`` (default: the same) the
+    query counts, the queries being the last positions.
+    """
     total = 0
-    for n in lengths:
-        total += int(visibility(int(n), int(n), window).sum()) if n else 0
+    q_lengths = lengths if q_lengths is None else q_lengths
+    for n, nq in zip(lengths, q_lengths):
+        if n and nq:
+            total += int(visibility(int(nq), int(n), window, int(n) - int(nq)).sum())
     return total

@@ -46,3 +46,43 @@ def brute_attention(q, k, v, cu, n_q_heads, n_kv_heads, scale, window):
                         acc += w * v[start + j][g][c]
                     out[t][h][c] = acc / z
     return out
+
+
+def brute_attention_chunked(q, k, v, cu_q, cu_k, n_q_heads, n_kv_heads, scale,
+                            window):
+    """Chunked prefill against a KV history, literal loops.
+
+    Sequence s has queries q[cu_q[s] .. cu_q[s+1]) and keys/values
+    k[cu_k[s] .. cu_k[s+1]); the queries are the last positions of the
+    sequence, so local query i is at position (Lk - Lq) + i.  A query with no
+    visible key gets a zero row.
+    """
+    total = len(q)
+    d_v = len(v[0][0]) if len(v) else 0
+    out = [[[0.0] * d_v for _ in range(n_q_heads)] for _ in range(total)]
+    for s in range(len(cu_q) - 1):
+        qa, qb = cu_q[s], cu_q[s + 1]
+        ka, kb = cu_k[s], cu_k[s + 1]
+        for t in range(qa, qb):
+            pos = (kb - ka) - (qb - qa) + (t - qa)
+            for h in range(n_q_heads):
+                g = (h * n_kv_heads) // n_q_heads
+                keys = [j for j in range(kb - ka)
+                        if j <= pos and not (window and pos - j >= window)]
+                if not keys:
+                    continue
+                scores = []
+                for j in keys:
+                    acc = 0.0
+                    for c in range(len(q[t][h])):
+                        acc += q[t][h][c] * k[ka + j][g][c]
+                    scores.append(scale * acc)
+                top = max(scores)
+                weights = [math.exp(x - top) for x in scores]
+                z = sum(weights)
+                for c in range(d_v):
+                    acc = 0.0
+                    for wgt, j in zip(weights, keys):
+                        acc += wgt * v[ka + j][g][c]
+                    out[t][h][c] = acc / z
+    return out

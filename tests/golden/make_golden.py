@@ -89,6 +89,51 @@ EXAMPLES = [
        [[[0.0]], [[0.75]], [[-3.0]]]),
 ]
 
+# Chunked prefill against a KV history: the queries are the last Lq of the
+# sequence's Lk positions, so a later chunk sees every earlier token (the
+# multi-chunk fix of atlas PR #69: kv_len = seq_len_start + n).
+
+
+def exk(name, why, cu_q, cu_k, hq, hkv, scale, window, q, k, v, out):
+    e = ex(name, why, cu_q, hq, hkv, scale, window, q, k, v, out)
+    e["cu_seqlens_k"] = cu_k
+    return e
+
+
+EXAMPLES += [
+    exk("history2_one_query",
+        "Lk=3, Lq=1: the query sits at position 2 and sees keys {0,1,2}, "
+        "scores [7, 0, ln2] -> (10 e^7 + 20 + 100)/(e^7 + 3)",
+        [0, 1], [0, 3], 1, 1, 1.0, 0,
+        [[[1.0]]], [[[7.0]], [[0.0]], [[LN2]]],
+        [[[10.0]], [[20.0]], [[50.0]]],
+        [[[(10 * E7 + 20 + 100) / (E7 + 3)]]]),
+    exk("history2_one_query_window2",
+        "Lk=3, Lq=1, W=2: position 2 sees keys {1,2}, scores [0, ln2] -> "
+        "(20 + 2*50)/3 = 40",
+        [0, 1], [0, 3], 1, 1, 1.0, 2,
+        [[[1.0]]], [[[7.0]], [[0.0]], [[LN2]]],
+        [[[10.0]], [[20.0]], [[50.0]]],
+        [[[40.0]]]),
+    exk("history1_chunk2",
+        "Lk=3, Lq=2: queries at positions 1 and 2; row 0 keys {0,1} scores "
+        "[7, 0] -> (10 e^7 + 20)/(e^7 + 1); row 1 keys {0,1,2} -> "
+        "(10 e^7 + 120)/(e^7 + 3)",
+        [0, 2], [0, 3], 1, 1, 1.0, 0,
+        [[[1.0]], [[1.0]]], [[[7.0]], [[0.0]], [[LN2]]],
+        [[[10.0]], [[20.0]], [[50.0]]],
+        [[[(10 * E7 + 20) / (E7 + 1)]], [[(10 * E7 + 120) / (E7 + 3)]]]),
+    exk("two_sequences_with_history",
+        "cu_q = [0,1,2], cu_k = [0,2,3]: sequence 0's query is position 1 "
+        "with scores [0, ln3] -> 3/4; sequence 1 has no history, its query "
+        "sees only its own key -> 2 (the score-100 key of sequence 0 is not "
+        "visible)",
+        [0, 1, 2], [0, 2, 3], 1, 1, 1.0, 0,
+        [[[1.0]], [[1.0]]], [[[0.0]], [[LN3]], [[0.0]]],
+        [[[0.0]], [[1.0]], [[2.0]]],
+        [[[0.75]], [[2.0]]]),
+]
+
 if __name__ == "__main__":
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "worked_examples.json")

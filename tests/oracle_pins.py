@@ -11,7 +11,10 @@ disagrees with:
   mean of the visible V rows, constant V, convex hull, shift invariance in
   K, packing and GQA replication),
 * torch's CPU float64 ``scaled_dot_product_attention`` as a second library
-  rendering of the causal case.
+  rendering of the causal case,
+* for chunked prefill against a KV history: the literal-loop brute force,
+  and the fact that running a sequence chunk by chunk against its growing
+  history reproduces the single-pass rows.
 """
 from __future__ import annotations
 
@@ -21,7 +24,7 @@ import os
 
 import numpy as np
 
-from bruteforce import brute_attention
+from bruteforce import brute_attention, brute_attention_chunked
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                       "worked_examples.json")
@@ -44,10 +47,17 @@ def pin_golden(mod):
     with open(GOLDEN) as f:
         examples = json.load(f)["examples"]
     for ex in examples:
-        got = mod.attention_varlen(np.array(ex["q"]), np.array(ex["k"]),
-                                   np.array(ex["v"]), ex["cu_seqlens"],
-                                   ex["n_q_heads"], ex["n_kv_heads"],
-                                   ex["scale"], ex["window"], workers=1)
+        if "cu_seqlens_k" in ex:
+            got = mod.attention_chunked(np.array(ex["q"]), np.array(ex["k"]),
+                                        np.array(ex["v"]), ex["cu_seqlens"],
+                                        ex["cu_seqlens_k"], ex["n_q_heads"],
+                                        ex["n_kv_heads"], ex["scale"],
+                                        ex["window"], workers=1)
+        else:
+            got = mod.attention_varlen(np.array(ex["q"]), np.array(ex["k"]),
+                                       np.array(ex["v"]), ex["cu_seqlens"],
+                                       ex["n_q_heads"], ex["n_kv_heads"],
+                                       ex["scale"], ex["window"], workers=1)
         want = np.array(ex["out"])
         assert got.shape == want.shape, ex["name"]
         err = np.max(np.abs(got - want))
@@ -228,6 +238,66 @@ def pin_parallel_equals_serial(mod):
     assert np.array_equal(a, b)
 
 
+CHUNK_CASES = [
+    # (q lengths, kv lengths), hq, hkv, d, window, scale
+    (([1], [6]), 1, 1, 2, 0, 0.8),
+    (([3], [8]), 2, 1, 3, 0, 0.6),
+    (([4], [4]), 2, 2, 2, 0, 0.9),
+    (([2, 0, 5], [7, 3, 5]), 4, 2, 4, 3, 0.5),
+    (([5, 1], [12, 1]), 2, 1, 2, 4, -0.7),
+    (([6], [15]), 4, 1, 8, 1, 0.3),
+    (([1, 2, 3], [9, 2, 10]), 4, 4, 2, 0, 1.1),
+]
+
+
+def _rand_chunked(rng, q_lengths, kv_lengths, hq, hkv, d):
+    return (rng.standard_normal((sum(q_lengths), hq, d)),
+            rng.standard_normal((sum(kv_lengths), hkv, d)),
+            rng.standard_normal((sum(kv_lengths), hkv, d)))
+
+
+def pin_chunked_bruteforce(mod):
+    for case_id, ((lq, lk), hq, hkv, d, w, scale) in enumerate(CHUNK_CASES):
+        rng = np.random.default_rng(300 + case_id)
+        q, k, v = _rand_chunked(rng, lq, lk, hq, hkv, d)
+        cq, ck = _cu(lq), _cu(lk)
+        want = np.array(brute_attention_chunked(
+            q.tolist(), k.tolist(), v.tolist(), cq, ck, hq, hkv, scale, w)
+        ).reshape(q.shape[0], hq, d)
+        got = mod.attention_chunked(q, k, v, cq, ck, hq, hkv, scale, w, workers=1)
+        err = np.max(np.abs(got - want)) if got.size else 0.0
+        assert err <= 1e-12, f"chunk case {case_id}: max err {err}"
+        rows = [(t, h) for t in range(q.shape[0]) for h in range(hq)]
+        if rows:
+            got_r = mod.attention_rows(q, k, v, cq, hq, hkv, scale, w, rows,
+                                       cu_seqlens_k=ck)
+            want_r = np.array([want[t, h] for t, h in rows])
+            assert np.max(np.abs(got_r - want_r)) <= 1e-12, f"chunk case {case_id} rows"
+
+
+def pin_chunks_reproduce_single_pass(mod):
+    # A sequence prefilled chunk by chunk, each chunk attending to the whole
+    # history before it, gives the rows of the single-pass prefill.
+    rng = np.random.default_rng(31)
+    n, hq, hkv, d = 57, 4, 2, 8
+    q, k, v = _rand(rng, [n], hq, hkv, d)
+    for w in (0, 5, 200):
+        full = mod.attention_varlen(q, k, v, [0, n], hq, hkv, 0.45, w, workers=1)
+        bounds = [0, 1, 9, 10, 33, 57]
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            got = mod.attention_chunked(q[a:b], k[:b], v[:b], [0, b - a], [0, b],
+                                        hq, hkv, 0.45, w, workers=1)
+            assert np.max(np.abs(got - full[a:b])) <= 1e-12, (w, a, b)
+        # the same chunks packed as one batch of three "sequences"
+        cq = [0, 9, 33, 57]
+        ck = [0, 9, 9 + 33, 9 + 33 + 57]
+        kk = np.concatenate([k[:9], k[:33], k[:57]])
+        vv = np.concatenate([v[:9], v[:33], v[:57]])
+        qq = np.concatenate([q[0:9], q[9:33], q[33:57]])
+        got = mod.attention_chunked(qq, kk, vv, cq, ck, hq, hkv, 0.45, w, workers=1)
+        assert np.max(np.abs(got - full)) <= 1e-12, w
+
+
 ALL_PINS = [
     pin_golden,
     pin_bruteforce,
@@ -242,4 +312,6 @@ ALL_PINS = [
     pin_gqa_equals_replicated,
     pin_sdpa_crosscheck,
     pin_parallel_equals_serial,
+    pin_chunked_bruteforce,
+    pin_chunks_reproduce_single_pass,
 ]

@@ -38,19 +38,25 @@ def failing_pins(mod):
 
 
 def _vis(op):
-    def visibility(n_rows, n_cols, window):
-        i = np.arange(n_rows)[:, None]
+    def visibility(n_rows, n_cols, window, q_offset=0):
+        i = q_offset + np.arange(n_rows)[:, None]
         j = np.arange(n_cols)[None, :]
         return op(i, j, window)
     return visibility
 
 
 def _probs(variant):
-    def softmax_probs(q_h, k_g, scale, window, _v=variant):
+    def softmax_probs(q_h, k_g, scale, window, q_offset=None, *, _v=variant):
         q_h = np.asarray(q_h, dtype=np.float64)
         k_g = np.asarray(k_g, dtype=np.float64)
-        n = q_h.shape[0]
-        vis = MUT_VIS_BASE(n, n, window)
+        n, nk = q_h.shape[0], k_g.shape[0]
+        if q_offset is None:
+            q_offset = nk - n
+        if _v == "history_ignored":
+            q_offset = 0
+        elif _v == "history_offset_plus_one":
+            q_offset = q_offset + 1 if nk > n else q_offset
+        vis = MUT_VIS_BASE(n, nk, window, q_offset)
         if _v == "transposed":
             s = scale * (k_g @ q_h.T)
         elif _v == "no_scale":
@@ -64,17 +70,19 @@ def _probs(variant):
         else:
             s = np.where(vis, s, -np.inf)
         m = s.max(axis=1, keepdims=True)
+        m = np.where(np.isfinite(m), m, 0.0)
         e = np.exp(s - m)
         if _v == "no_normalise":
             return e
         if _v == "normalise_columns":
             return e / e.sum(axis=0, keepdims=True)
-        return e / e.sum(axis=1, keepdims=True)
+        z = e.sum(axis=1, keepdims=True)
+        return e / np.where(z > 0, z, 1.0)
     return softmax_probs
 
 
-def MUT_VIS_BASE(n_rows, n_cols, window):
-    i = np.arange(n_rows)[:, None]
+def MUT_VIS_BASE(n_rows, n_cols, window, q_offset=0):
+    i = q_offset + np.arange(n_rows)[:, None]
     j = np.arange(n_cols)[None, :]
     vis = j <= i
     if window > 0:
@@ -89,6 +97,23 @@ def _no_isolation(mod):
         cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
         return base(q, k, v, [0, cu[-1]], hq, hkv, scale, window, workers=workers)
     return attention_varlen
+
+
+def _chunk_keys_only(mod):
+    base = mod.attention_chunked
+
+    def attention_chunked(q, k, v, cu_q, cu_k, hq, hkv, scale, window, workers=None):
+        # keeps only the chunk's own keys: the last Lq of each sequence
+        cq = [int(x) for x in np.asarray(cu_q).reshape(-1)]
+        ck = [int(x) for x in np.asarray(cu_k).reshape(-1)]
+        idx = []
+        for s in range(len(cq) - 1):
+            lq = cq[s + 1] - cq[s]
+            idx.extend(range(ck[s + 1] - lq, ck[s + 1]))
+        k2 = np.asarray(k)[idx]
+        v2 = np.asarray(v)[idx]
+        return base(q, k2, v2, cq, cq, hq, hkv, scale, window, workers=workers)
+    return attention_chunked
 
 
 MUTANTS = {
@@ -111,6 +136,9 @@ MUTANTS = {
     "softmax_not_normalised": ("softmax_probs", _probs("no_normalise")),
     "softmax_normalised_over_queries": ("softmax_probs", _probs("normalise_columns")),
     "sequences_not_isolated": ("attention_varlen", None),
+    "history_ignored": ("softmax_probs", _probs("history_ignored")),
+    "history_offset_plus_one": ("softmax_probs", _probs("history_offset_plus_one")),
+    "chunk_sees_only_its_own_keys": ("attention_chunked", None),
 }
 
 
@@ -124,5 +152,7 @@ def test_mutant_is_caught(name):
     attr, repl = MUTANTS[name]
     if name == "sequences_not_isolated":
         repl = _no_isolation(mod)
+    if name == "chunk_sees_only_its_own_keys":
+        repl = _chunk_keys_only(mod)
     setattr(mod, attr, repl)
     assert failing_pins(mod), f"mutant {name} passed every pin"
