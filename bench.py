@@ -86,11 +86,16 @@ def cpu_baseline(w, inp, n_heads_sample: int):
     k = inp["k"][:, :n_kv]
     v = inp["v"][:, :n_kv]
     threads = host_threads()
+    kv_lengths = inp.get("kv_lengths")
     t0 = time.perf_counter()
-    oracle.attention_varlen(q, k, v, inp["cu_seqlens"], hs, n_kv, w.attn_scale,
-                            w.window, workers=threads)
+    if kv_lengths is None:
+        oracle.attention_varlen(q, k, v, inp["cu_seqlens"], hs, n_kv, w.attn_scale,
+                                w.window, workers=threads)
+    else:
+        oracle.attention_chunked(q, k, v, inp["cu_seqlens"], inp["cu_seqlens_k"], hs,
+                                 n_kv, w.attn_scale, w.window, workers=threads)
     dt = time.perf_counter() - t0
-    flops = measure.causal_flops(inp["lengths"], hs, w.head_dim, w.window)
+    flops = measure.causal_flops(inp["lengths"], hs, w.head_dim, w.window, kv_lengths)
     jobs = hs * sum(1 for n in inp["lengths"] if n > 0)
     return {
         "value": flops / dt / 1e12,
@@ -159,13 +164,20 @@ def main():
     k = inp["k"].to(dev)
     v = inp["v"].to(dev)
     cu = inp["cu_seqlens"].to(dev)
+    kv_lengths = inp.get("kv_lengths")
+    cuk = inp["cu_seqlens_k"].to(dev) if kv_lengths is not None else None
     out = torch.empty(q.shape[0], w.n_q_heads, w.head_dim, dtype=torch.bfloat16,
                       device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        binding.attn_prefill(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads,
-                             w.head_dim, w.attn_scale, w.window, stream=stream)
+        if cuk is None:
+            binding.attn_prefill(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads,
+                                 w.head_dim, w.attn_scale, w.window, stream=stream)
+        else:
+            binding.attn_prefill_chunked(q, k, v, out, cu, cuk, w.n_q_heads,
+                                         w.n_kv_heads, w.head_dim, w.attn_scale,
+                                         w.window, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -185,7 +197,7 @@ def main():
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
     avg_ms = sum(durs) / len(durs)
 
-    flops = measure.causal_flops(lengths, w.n_q_heads, w.head_dim, w.window)
+    flops = measure.causal_flops(lengths, w.n_q_heads, w.head_dim, w.window, kv_lengths)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
@@ -211,6 +223,7 @@ def main():
             "workload": name,
             "seq_lens": lengths if len(lengths) <= 16 else f"{len(lengths)} seqs",
             "tokens": int(sum(lengths)),
+            **({"kv_history": list(w.history)} if w.history else {}),
             "n_q_heads": w.n_q_heads,
             "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim,
@@ -231,7 +244,8 @@ def main():
             "kernel_avg_us": round(avg_ms * 1e3, 2),
             "kernel_min_us": round(durs[0] * 1e3, 2),
             "algorithmic_bytes": measure.algorithmic_bytes(
-                lengths, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype),
+                lengths, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype,
+                kv_lengths),
         },
         "cpu_baseline": None,
     }

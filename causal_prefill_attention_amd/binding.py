@@ -23,7 +23,7 @@ ATTN_FP16 = 1
 ATTN_FP32 = 2
 
 #: Every symbol include/attn_prefill.h declares.
-EXPORTS = ("attn_prefill", "attn_prefill_status_string",
+EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_status_string",
            "attn_prefill_last_error", "attn_prefill_supported_head_dims",
            "attn_prefill_version")
 
@@ -66,6 +66,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
         ctypes.POINTER(AttnSeqlens), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_prefill_chunked.restype = ctypes.c_int
+    lib.attn_prefill_chunked.argtypes = [
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnSeqlens), ctypes.POINTER(AttnSeqlens), ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
     lib.attn_prefill_status_string.restype = ctypes.c_char_p
     lib.attn_prefill_status_string.argtypes = [ctypes.c_int]
     lib.attn_prefill_last_error.restype = ctypes.c_char_p
@@ -104,6 +110,19 @@ def call_raw(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
                             ctypes.c_void_p(stream))
 
 
+def call_raw_chunked(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
+                     seqlens_q: AttnSeqlens, seqlens_k: AttnSeqlens, n_q_heads: int,
+                     n_kv_heads: int, head_dim: int, scale: float,
+                     sliding_window: int, stream: Optional[int] = None) -> int:
+    """Calls ``attn_prefill_chunked`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_prefill_chunked(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(out),
+        ctypes.byref(seqlens_q), ctypes.byref(seqlens_k), int(n_q_heads),
+        int(n_kv_heads), int(head_dim), float(scale), int(sliding_window),
+        ctypes.c_void_p(stream))
+
+
 def _dtype_code(t) -> int:
     import torch
 
@@ -136,18 +155,46 @@ def attn_prefill(q, k, v, out, cu_seqlens, n_q_heads: int, n_kv_heads: int,
     tensor of n_seqs + 1 offsets.  ``stream`` defaults to torch's current
     stream on q's device.
     """
-    import torch
-
-    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be an int32 GPU tensor")
-    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2 or cu_seqlens.stride(0) != 1:
-        raise ValueError("cu_seqlens must be a contiguous 1-D tensor of n_seqs + 1")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
-    seq = AttnSeqlens(cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, 0)
+    seq = _seqlens(cu_seqlens, "cu_seqlens")
     status = call_raw(describe(q), describe(k), describe(v), describe(out), seq,
                       n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
-                      handle)
+                      _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
+
+
+def attn_prefill_chunked(q, k, v, out, cu_seqlens_q, cu_seqlens_k, n_q_heads: int,
+                         n_kv_heads: int, head_dim: int, scale: float,
+                         sliding_window: int = 0, stream=None) -> None:
+    """Chunked prefill against a KV history; ``out`` is written in place.
+
+    q, out: [Tq, heads, head_dim] packed by ``cu_seqlens_q``; k, v:
+    [Tk, n_kv_heads, head_dim] packed by ``cu_seqlens_k`` (same number of
+    sequences, each sequence's keys being its history followed by its new
+    tokens).
+    """
+    sq = _seqlens(cu_seqlens_q, "cu_seqlens_q")
+    sk = _seqlens(cu_seqlens_k, "cu_seqlens_k")
+    status = call_raw_chunked(describe(q), describe(k), describe(v), describe(out),
+                              sq, sk, n_q_heads, n_kv_heads, head_dim, scale,
+                              sliding_window, _stream_handle(q, stream))
+    if status != ATTN_OK:
+        raise AttnPrefillError(status, last_error())
+
+
+def _seqlens(cu, name: str) -> AttnSeqlens:
+    import torch
+
+    if not cu.is_cuda or cu.dtype != torch.int32:
+        raise ValueError(f"{name} must be an int32 GPU tensor")
+    if cu.dim() != 1 or cu.numel() < 2 or cu.stride(0) != 1:
+        raise ValueError(f"{name} must be a contiguous 1-D tensor of n_seqs + 1")
+    return AttnSeqlens(cu.data_ptr(), cu.numel() - 1, 0)
+
+
+def _stream_handle(q, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream

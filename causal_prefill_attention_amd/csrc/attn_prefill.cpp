@@ -94,32 +94,61 @@ int check_tensor(const attn_tensor* t, const char* what, int32_t n_heads, int32_
   return ATTN_OK;
 }
 
-int debug_validate_offsets(const attn_seqlens* cu, int64_t n_tokens, hipStream_t stream) {
-  std::vector<int32_t> host((size_t)cu->n_seqs + 1);
+int read_offsets(const attn_seqlens* cu, std::vector<int32_t>& host, hipStream_t stream,
+                 const char* what) {
+  host.resize((size_t)cu->n_seqs + 1);
   hipError_t e = hipStreamSynchronize(stream);
   if (e == hipSuccess)
     e = hipMemcpy(host.data(), cu->data, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost);
   if (e != hipSuccess)
-    return fail(ATTN_ERR_HIP, "ATTN_PREFILL_VALIDATE: reading cu_seqlens failed: %s",
+    return fail(ATTN_ERR_HIP, "ATTN_PREFILL_VALIDATE: reading %s failed: %s", what,
                 hipGetErrorString(e));
-  if (host[0] != 0) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", host[0]);
-  for (size_t i = 1; i < host.size(); ++i)
-    if (host[i] < host[i - 1])
-      return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens decreases at index %zu", i);
-  if (host.back() != n_tokens)
-    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens[n_seqs] = %d, expected n_tokens = %lld",
-                host.back(), (long long)n_tokens);
   return ATTN_OK;
 }
 
-}  // namespace
+int check_offsets(const std::vector<int32_t>& host, int64_t n_tokens, const char* what) {
+  if (host[0] != 0) return fail(ATTN_ERR_INVALID_ARG, "%s[0] = %d, expected 0", what, host[0]);
+  for (size_t i = 1; i < host.size(); ++i)
+    if (host[i] < host[i - 1])
+      return fail(ATTN_ERR_INVALID_ARG, "%s decreases at index %zu", what, i);
+  if (host.back() != n_tokens)
+    return fail(ATTN_ERR_INVALID_ARG, "%s[n_seqs] = %d, expected %lld", what, host.back(),
+                (long long)n_tokens);
+  return ATTN_OK;
+}
 
-extern "C" {
+// Debug-only host check of the device offsets (ATTN_PREFILL_VALIDATE=1).
+int debug_validate_offsets(const attn_seqlens* cu_q, int64_t n_q, const attn_seqlens* cu_k,
+                           int64_t n_k, hipStream_t stream) {
+  std::vector<int32_t> hq, hk;
+  int rc;
+  if ((rc = read_offsets(cu_q, hq, stream, "cu_seqlens")) != ATTN_OK) return rc;
+  if ((rc = check_offsets(hq, n_q, "cu_seqlens")) != ATTN_OK) return rc;
+  if (cu_k == nullptr) return ATTN_OK;
+  if ((rc = read_offsets(cu_k, hk, stream, "cu_seqlens_k")) != ATTN_OK) return rc;
+  if ((rc = check_offsets(hk, n_k, "cu_seqlens_k")) != ATTN_OK) return rc;
+  for (size_t s = 0; s + 1 < hq.size(); ++s)
+    if (hq[s + 1] - hq[s] > hk[s + 1] - hk[s])
+      return fail(ATTN_ERR_INVALID_ARG, "sequence %zu has %d queries but only %d keys", s,
+                  hq[s + 1] - hq[s], hk[s + 1] - hk[s]);
+  return ATTN_OK;
+}
 
-int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
-                 const attn_tensor* out, const attn_seqlens* cu_seqlens,
-                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
-                 int32_t sliding_window, attn_stream_t stream) {
+int check_seqlens(const attn_seqlens* cu, const char* what) {
+  if (cu == nullptr) return fail(ATTN_ERR_INVALID_ARG, "%s is NULL", what);
+  if (cu->n_seqs < 1) return fail(ATTN_ERR_INVALID_ARG, "%s: n_seqs %d < 1", what, (int)cu->n_seqs);
+  if (cu->data == nullptr) return fail(ATTN_ERR_INVALID_ARG, "%s data is NULL", what);
+  if (cu->max_seqlen < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "%s: max_seqlen %d < 0", what, (int)cu->max_seqlen);
+  return ATTN_OK;
+}
+
+// Both entry points: cu_k == nullptr means the keys are the queries' own
+// tokens (no history).
+int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                const attn_tensor* out, const attn_seqlens* cu_q, const attn_seqlens* cu_k,
+                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                int32_t sliding_window, attn_stream_t stream) {
   g_last_error.clear();
   if (n_q_heads < 1 || n_kv_heads < 1)
     return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
@@ -146,21 +175,34 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
     return fail(ATTN_ERR_UNSUPPORTED, "k/v dtype must be BF16 or FP16");
   if (out->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "out dtype must be BF16");
   const int64_t T = q->n_tokens;
-  if (k->n_tokens != T || v->n_tokens != T || out->n_tokens != T)
-    return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: q %lld k %lld v %lld out %lld",
-                (long long)T, (long long)k->n_tokens, (long long)v->n_tokens,
-                (long long)out->n_tokens);
-  if (cu_seqlens == nullptr) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens is NULL");
-  if (cu_seqlens->n_seqs < 1)
-    return fail(ATTN_ERR_INVALID_ARG, "n_seqs %d < 1", (int)cu_seqlens->n_seqs);
-  if (cu_seqlens->data == nullptr)
-    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens data is NULL");
-  if (cu_seqlens->max_seqlen < 0)
-    return fail(ATTN_ERR_INVALID_ARG, "max_seqlen %d < 0", (int)cu_seqlens->max_seqlen);
+  const int64_t Tk = k->n_tokens;
+  if (cu_k == nullptr) {
+    if (k->n_tokens != T || v->n_tokens != T || out->n_tokens != T)
+      return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: q %lld k %lld v %lld out %lld",
+                  (long long)T, (long long)k->n_tokens, (long long)v->n_tokens,
+                  (long long)out->n_tokens);
+  } else {
+    if (out->n_tokens != T)
+      return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: q %lld out %lld", (long long)T,
+                  (long long)out->n_tokens);
+    if (v->n_tokens != Tk)
+      return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: k %lld v %lld", (long long)Tk,
+                  (long long)v->n_tokens);
+  }
+  if ((rc = check_seqlens(cu_q, "cu_seqlens")) != ATTN_OK) return rc;
+  if (cu_k != nullptr) {
+    if ((rc = check_seqlens(cu_k, "cu_seqlens_k")) != ATTN_OK) return rc;
+    if (cu_k->n_seqs != cu_q->n_seqs)
+      return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens has %d sequences, cu_seqlens_k %d",
+                  (int)cu_q->n_seqs, (int)cu_k->n_seqs);
+    if (T > 0 && Tk == 0)
+      return fail(ATTN_ERR_INVALID_ARG, "q has %lld tokens but k and v have none",
+                  (long long)T);
+  }
   // K and V tiles are read through buffer resources with a 32-bit range and
   // 32-bit offsets, one resource per tile of up to 64 rows.
   for (const attn_tensor* t : {k, v}) {
-    if (T > 1 && t->token_stride * elem_bytes(t->dtype) * 64 > (int64_t)INT32_MAX)
+    if (Tk > 1 && t->token_stride * elem_bytes(t->dtype) * 64 > (int64_t)INT32_MAX)
       return fail(ATTN_ERR_UNSUPPORTED,
                   "%s: token stride of %lld bytes is too large (at most 32 MiB - 1 B)",
                   t == k ? "k" : "v", (long long)(t->token_stride * elem_bytes(t->dtype)));
@@ -173,7 +215,7 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
     return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
 
   const int bm = attnp::prefill_min_block_m(head_dim);
-  const int64_t slots = (T + bm - 1) / bm + cu_seqlens->n_seqs;
+  const int64_t slots = (T + bm - 1) / bm + cu_q->n_seqs;
   const int64_t blocks = slots * n_q_heads;
   if (slots > INT32_MAX || blocks * 1024 >= ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large",
@@ -181,7 +223,9 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
 
   const char* dbg = getenv("ATTN_PREFILL_VALIDATE");
   if (dbg != nullptr && dbg[0] == '1') {
-    if ((rc = debug_validate_offsets(cu_seqlens, T, stream)) != ATTN_OK) return rc;
+    if ((rc = debug_validate_offsets(cu_q, T, cu_k, Tk, reinterpret_cast<hipStream_t>(stream))) !=
+        ATTN_OK)
+      return rc;
   }
 
   attnp::PrefillParams p;
@@ -189,7 +233,8 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
   p.k = k->data;
   p.v = v->data;
   p.out = out->data;
-  p.cu_seqlens = cu_seqlens->data;
+  p.cu_seqlens = cu_q->data;
+  p.cu_seqlens_k = cu_k != nullptr ? cu_k->data : cu_q->data;
   p.q_ts = q->token_stride;
   p.q_hs = q->head_stride;
   p.k_ts = k->token_stride;
@@ -199,7 +244,8 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
   p.o_ts = out->token_stride;
   p.o_hs = out->head_stride;
   p.n_tokens = (int32_t)T;
-  p.n_seqs = cu_seqlens->n_seqs;
+  p.n_tokens_k = (int32_t)Tk;
+  p.n_seqs = cu_q->n_seqs;
   p.n_q_heads = n_q_heads;
   p.group = n_q_heads / n_kv_heads;
   p.window = sliding_window;
@@ -218,6 +264,31 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
   if (e != hipSuccess)
     return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                 const attn_tensor* out, const attn_seqlens* cu_seqlens,
+                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                 int32_t sliding_window, attn_stream_t stream) {
+  return run_prefill(q, k, v, out, cu_seqlens, nullptr, n_q_heads, n_kv_heads, head_dim, scale,
+                     sliding_window, stream);
+}
+
+int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                         const attn_tensor* out, const attn_seqlens* cu_seqlens_q,
+                         const attn_seqlens* cu_seqlens_k, int32_t n_q_heads,
+                         int32_t n_kv_heads, int32_t head_dim, float scale,
+                         int32_t sliding_window, attn_stream_t stream) {
+  if (cu_seqlens_k == nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
+  }
+  return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, n_q_heads, n_kv_heads, head_dim,
+                     scale, sliding_window, stream);
 }
 
 const char* attn_prefill_status_string(int status) {

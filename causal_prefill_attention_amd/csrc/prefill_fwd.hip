@@ -4,7 +4,11 @@
 //   out[i,h] = sum_j softmax_j(scale * q[i,h] . k[j,g]) v[j,g],
 //   j visible iff j <= i (causal bound kv_end = min(q_pos + 1, seq_len), atlas
 //   PR #69 fused MLA prefill) and, for a window W > 0, j >= i - W + 1 (the W
-//   most recent keys, m40-llm AGENTS.md "Current Progress").  The softmax is
+//   most recent keys, m40-llm AGENTS.md "Current Progress").  With a KV
+//   history (chunked prefill: a later chunk attends to every earlier token,
+//   kv_len = seq_len_start + n in atlas PR #69) the sequence has Lk keys and
+//   Lq <= Lk queries, the queries being its last Lq positions: i above is
+//   the query's key position Lk - Lq + (local query index).  The softmax is
 //   evaluated online over key tiles with a running max and running sum (the
 //   fused MLA prefill kernel's recurrence in atlas PR #69), in base 2 with
 //   log2(e) folded into the score multiplier.
@@ -152,25 +156,30 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ------------------------------------------------------------- work decode
 struct Work {
-  int start;  // first token of the sequence in the packed batch
-  int len;    // sequence length
-  int q0;     // first local query row of this tile
+  int start;   // first query token of the sequence in the packed q / out
+  int len;     // number of queries (new tokens) of the sequence
+  int kstart;  // first key token of the sequence in the packed k / v
+  int klen;    // number of keys: the history followed by the new tokens
+  int q0;      // first local query row of this tile
   bool valid;
 };
 
 // Maps a q-tile slot to (sequence, tile).  Slots enumerate sequences in
 // order; inside a sequence the last (most expensive causal) tile comes
-// first.  Every lane of the wave computes the same answer.
+// first.  Query and key offsets are clamped into [0, T].  Every lane of the
+// wave computes the same answer.
 template <int BM>
 __device__ Work decode_work(const PrefillParams& p, int slot) {
   const int lane = threadIdx.x & (kWave - 1);
   int base = 0;
   for (int s0 = 0; s0 < p.n_seqs; s0 += kWave) {
     const int s = s0 + lane;
-    int a = 0, b = 0;
+    int a = 0, b = 0, ka = 0, kb = 0;
     if (s < p.n_seqs) {
       a = min(max(p.cu_seqlens[s], 0), p.n_tokens);
       b = min(max(p.cu_seqlens[s + 1], 0), p.n_tokens);
+      ka = min(max(p.cu_seqlens_k[s], 0), p.n_tokens_k);
+      kb = min(max(p.cu_seqlens_k[s + 1], 0), p.n_tokens_k);
     }
     const int len = max(b - a, 0);
     const int nt = (len + BM - 1) / BM;
@@ -188,6 +197,8 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
       Work w;
       w.start = __shfl(a, src, kWave);
       w.len = __shfl(len, src, kWave);
+      w.kstart = __shfl(ka, src, kWave);
+      w.klen = __shfl(max(kb - ka, 0), src, kWave);
       const int ntiles = __shfl(nt, src, kWave);
       const int rank = slot - base - excl;  // 0 = heaviest tile
       w.q0 = (ntiles - 1 - rank) * BM;
@@ -196,7 +207,7 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
     }
     base += total;
   }
-  Work w{0, 0, 0, false};
+  Work w{0, 0, 0, 0, 0, false};
   return w;
 }
 
@@ -222,13 +233,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   w.start = __builtin_amdgcn_readfirstlane(w.start);
   w.len = __builtin_amdgcn_readfirstlane(w.len);
   w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
+  w.kstart = __builtin_amdgcn_readfirstlane(w.kstart);
+  w.klen = __builtin_amdgcn_readfirstlane(w.klen);
 
   const int kvh = head / p.group;
+  // Queries are the last len of the sequence's klen positions: local query
+  // i sits at key position hist + i (hist = 0 without a KV history).
+  const int hist = w.klen - w.len;
   const int q_end = min(w.len, w.q0 + kBM);
-  const int kv_hi = q_end;  // the tile's last query sees keys < q_end
-  const int kv_lo = p.window > 0 ? max(0, w.q0 - p.window + 1) : 0;
+  // the tile's last query sees keys < hist + q_end
+  const int kv_hi = min(max(hist + q_end, 0), w.klen);
+  const int kv_lo = p.window > 0 ? min(max(0, hist + w.q0 - p.window + 1), kv_hi) : 0;
   const int kv_start = kv_lo - kv_lo % kBN;
-  const int n_tiles = (kv_hi - kv_start + kBN - 1) / kBN;
+  // at least one (then fully masked) tile keeps the slot schedule uniform
+  // when no key is visible, which only malformed offsets produce
+  const int n_tiles = max(1, (kv_hi - kv_start + kBN - 1) / kBN);
 
   const int col = lane & 31;   // query column of this lane
   const int half = lane >> 5;  // which 8-wide half of each 16-wide k-step
@@ -236,6 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int wq_last = min(wq0 + 31, w.len - 1);
   const bool wave_live = wq0 < w.len;
   const int myq = wq0 + col;
+  const int mypos = hist + myq;  // key position of this lane's query
 
   // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7].
   bf16x8_t qf[C::DCH];
@@ -262,9 +282,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   // ---- K/V tile movement (K by group A, V by group B).  Per-sequence bases
   // are wave-uniform; each tile is read through a buffer resource covering
   // only its valid rows.
-  const kvelem* kseq = static_cast<const kvelem*>(p.k) + (int64_t)w.start * p.k_ts +
+  const kvelem* kseq = static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts +
                        (int64_t)kvh * p.k_hs;
-  const kvelem* vseq = static_cast<const kvelem*>(p.v) + (int64_t)w.start * p.v_ts +
+  const kvelem* vseq = static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts +
                        (int64_t)kvh * p.v_hs;
   const int k_row_bytes = (int)(p.k_ts * (int64_t)sizeof(kvelem));
   const int v_row_bytes = (int)(p.v_ts * (int64_t)sizeof(kvelem));
@@ -354,7 +374,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 
   // Whether every key of the tile at kv0 is visible to every row of this wave.
   auto tile_full = [&](int kv0) {
-    return (kv0 + kBN - 1 <= wq0) && (p.window == 0 || kv0 >= wq_last - p.window + 1);
+    return (kv0 + kBN - 1 <= hist + wq0) &&
+           (p.window == 0 || kv0 >= hist + wq_last - p.window + 1);
   };
 
   // S^T = K Q^T for the tile in K stage `st`.
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key <= myq && (p.window == 0 || key > myq - p.window);
+          const bool vis = key <= mypos && (p.window == 0 || key > mypos - p.window);
           if (!vis) s[kb][r] = -INFINITY;
         }
       }
@@ -566,7 +587,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     constexpr int OSTR = HDIM + 8;  // row pitch in LDS (bf16 elements)
     static_assert(kWaves * 32 * OSTR <= 2 * C::K_ELEMS + 2 * C::V_ELEMS, "O slices fit");
     uint16_t* ob = smem + wave * 32 * OSTR;
-    const float inv = 1.f / l_tot;  // rows past the sequence are never stored
+    // rows past the sequence are never stored; a row without any visible
+    // key (malformed offsets only) is written as zeros
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int c = 0; c < C::DBLK; ++c) {
 #pragma unroll

@@ -16,12 +16,14 @@ struct PrefillParams {
   const void* k;
   const void* v;
   void* out;
-  const int32_t* cu_seqlens;  // device, n_seqs + 1 entries
+  const int32_t* cu_seqlens;    // device, n_seqs + 1 query offsets
+  const int32_t* cu_seqlens_k;  // device, n_seqs + 1 key offsets (may equal cu_seqlens)
   int64_t q_ts, q_hs;         // token / head strides
   int64_t k_ts, k_hs;
   int64_t v_ts, v_hs;
   int64_t o_ts, o_hs;
-  int32_t n_tokens;           // T (offsets are clamped into [0, T])
+  int32_t n_tokens;           // Tq: tokens of q and out (query offsets clamp into [0, Tq])
+  int32_t n_tokens_k;         // Tk: tokens of k and v (key offsets clamp into [0, Tk])
   int32_t n_seqs;
   int32_t n_q_heads;
   int32_t group;              // n_q_heads / n_kv_heads

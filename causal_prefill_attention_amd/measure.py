@@ -11,7 +11,7 @@ dtype, and the bf16 output written once.
 """
 from __future__ import annotations
 
-from typing import Sequence
+from typing import Optional, Sequence
 
 #: MI355X dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
@@ -30,19 +30,42 @@ def visible_pairs_one(n: int, window: int) -> int:
     return window * (window + 1) // 2 + (n - window) * window
 
 
-def visible_pairs(lengths: Sequence[int], window: int) -> int:
-    return sum(visible_pairs_one(int(n), window) for n in lengths)
+def _prefix_visible(p: int, window: int) -> int:
+    """Visible keys summed over the queries at positions 0 .. p - 1."""
+    if p <= 0:
+        return 0
+    if window <= 0 or window >= p:
+        return p * (p + 1) // 2
+    return window * (window + 1) // 2 + (p - window) * window
+
+
+def visible_pairs_history(n_q: int, n_k: int, window: int) -> int:
+    """Visible pairs when the n_q queries are the last positions of n_k."""
+    if n_q <= 0 or n_k <= 0:
+        return 0
+    first = max(n_k - n_q, 0)  # positions below 0 see nothing
+    return _prefix_visible(n_k, window) - _prefix_visible(first, window)
+
+
+def visible_pairs(lengths: Sequence[int], window: int,
+                  kv_lengths: Optional[Sequence[int]] = None) -> int:
+    if kv_lengths is None:
+        return sum(visible_pairs_one(int(n), window) for n in lengths)
+    return sum(visible_pairs_history(int(n), int(m), window)
+               for n, m in zip(lengths, kv_lengths))
 
 
 def causal_flops(lengths: Sequence[int], n_q_heads: int, head_dim: int,
-                 window: int) -> int:
-    return 4 * head_dim * n_q_heads * visible_pairs(lengths, window)
+                 window: int, kv_lengths: Optional[Sequence[int]] = None) -> int:
+    return 4 * head_dim * n_q_heads * visible_pairs(lengths, window, kv_lengths)
 
 
 def algorithmic_bytes(lengths: Sequence[int], n_q_heads: int, n_kv_heads: int,
-                      head_dim: int, q_dtype: str, kv_dtype: str) -> int:
+                      head_dim: int, q_dtype: str, kv_dtype: str,
+                      kv_lengths: Optional[Sequence[int]] = None) -> int:
     t = int(sum(lengths))
+    tk = t if kv_lengths is None else int(sum(kv_lengths))
     q = t * n_q_heads * head_dim * DTYPE_BYTES[q_dtype]
-    kv = 2 * t * n_kv_heads * head_dim * DTYPE_BYTES[kv_dtype]
+    kv = 2 * tk * n_kv_heads * head_dim * DTYPE_BYTES[kv_dtype]
     o = t * n_q_heads * head_dim * 2
     return q + kv + o

@@ -18,6 +18,10 @@ Recipe (the same for every workload):
 
 The packed layout is ``[T, heads, head_dim]`` with the sequences stored one
 after another; ``cu_seqlens`` holds the ``n_seqs + 1`` cumulative offsets.
+A chunked-prefill workload gives each sequence a KV history: its K/V hold
+``history + length`` tokens (packed by ``cu_seqlens_k``) and its Q only the
+``length`` new ones; K and V are then drawn with ``Tk`` rows instead of
+``T``, in the same order.
 This matches the per-layer KV addressing ``[sequence][position][kv_head]
 [head_dim]`` and the packed offsets of the m40-llm AGENTS.md page ("Project
 Snapshot" and the varlen-batch task), with one layer's slice taken.
@@ -56,6 +60,7 @@ class Workload:
     k_outlier_frac: float = 0.0
     k_outlier_mult: float = 30.0
     scale: Optional[float] = None  # None -> 1/sqrt(head_dim)
+    history: Optional[Tuple[int, ...]] = None  # KV history per sequence (chunked)
 
     @property
     def attn_scale(self) -> float:
@@ -75,6 +80,7 @@ class Workload:
             "kv_dtype": self.kv_dtype,
             "k_outlier_frac": self.k_outlier_frac,
             "scale": self.attn_scale,
+            **({"history": list(self.history)} if self.history else {}),
         }
 
 
@@ -106,6 +112,15 @@ WORKLOADS: Dict[str, Workload] = {
     "long_8192tok_4q1kv_outliers_share": Workload(
         "long_8192tok_4q1kv_outliers_share", 4, (8192,), 4, 1, _D,
         k_outlier_frac=0.01, scale=_SCALE),
+    # chunked prefill: the last 2048 tokens of an 8192-token sequence against
+    # its 6144-token KV history
+    "chunk2048_hist6144_32q1kv_outliers": Workload(
+        "chunk2048_hist6144_32q1kv_outliers", 5, (2048,), 32, 1, _D,
+        k_outlier_frac=0.01, scale=_SCALE, history=(6144,)),
+    # a packed batch of chunks with ragged histories, GQA 4:1
+    "chunks8_gqa32q8kv_history": Workload(
+        "chunks8_gqa32q8kv_history", 6, (300, 1, 64, 1000, 129, 0, 77, 512),
+        32, 8, _D, scale=_SCALE, history=(700, 4000, 0, 24, 2000, 50, 3, 1536)),
 }
 
 #: The workload the throughput metric is quoted on.
@@ -115,12 +130,14 @@ HEADLINE = "long_8192tok_32q1kv_outliers"
 def custom(name: str, lengths: Sequence[int], n_q_heads: int, n_kv_heads: int,
            head_dim: int = _D, window: int = 0, q_dtype: str = "bf16",
            kv_dtype: str = "bf16", seed: int = 0, scale: Optional[float] = None,
-           k_outlier_frac: float = 0.0) -> Workload:
-    """A test-sized workload with explicit lengths."""
+           k_outlier_frac: float = 0.0,
+           history: Optional[Sequence[int]] = None) -> Workload:
+    """A test-sized workload with explicit lengths (and KV histories)."""
     return Workload(name, seed, tuple(int(x) for x in lengths), n_q_heads,
                     n_kv_heads, head_dim, window=window, q_dtype=q_dtype,
                     kv_dtype=kv_dtype, scale=scale,
-                    k_outlier_frac=k_outlier_frac)
+                    k_outlier_frac=k_outlier_frac,
+                    history=None if history is None else tuple(int(x) for x in history))
 
 
 def draw_lengths(w: Workload, rng: np.random.Generator) -> List[int]:
@@ -147,15 +164,23 @@ def make_inputs(w: Workload) -> Dict[str, object]:
 
     Returns ``q``, ``k``, ``v`` (torch CPU tensors, contiguous
     ``[T, heads, head_dim]``), ``cu_seqlens`` (torch int32 CPU), ``lengths``
-    and a SHA-256 per tensor.
+    and a SHA-256 per tensor; with a KV history also ``cu_seqlens_k`` and
+    ``kv_lengths`` (K and V then have ``Tk`` rows).
     """
     rng = np.random.default_rng(w.seed)
     lengths = draw_lengths(w, rng)
     total = int(sum(lengths))
+    if w.history is not None:
+        if len(w.history) != len(lengths):
+            raise ValueError("history needs one entry per sequence")
+        kv_lengths = [int(h) + int(n) for h, n in zip(w.history, lengths)]
+    else:
+        kv_lengths = list(lengths)
+    total_k = int(sum(kv_lengths))
     d = w.head_dim
     q64 = rng.standard_normal((total, w.n_q_heads, d))
-    k64 = rng.standard_normal((total, w.n_kv_heads, d))
-    v64 = rng.standard_normal((total, w.n_kv_heads, d))
+    k64 = rng.standard_normal((total_k, w.n_kv_heads, d))
+    v64 = rng.standard_normal((total_k, w.n_kv_heads, d))
     if w.k_outlier_frac > 0.0 and k64.size > 0:
         n_out = int(math.floor(w.k_outlier_frac * k64.size))
         idx = rng.choice(k64.size, size=n_out, replace=False)
@@ -165,11 +190,17 @@ def make_inputs(w: Workload) -> Dict[str, object]:
     k = torch.from_numpy(k64).to(_TORCH_DTYPES[w.kv_dtype])
     v = torch.from_numpy(v64).to(_TORCH_DTYPES[w.kv_dtype])
     cu = torch.from_numpy(cu_seqlens_of(lengths))
-    return {
+    out = {
         "q": q, "k": k, "v": v, "cu_seqlens": cu, "lengths": lengths,
         "sha256": {"q": sha256_of(q), "k": sha256_of(k), "v": sha256_of(v),
                    "cu_seqlens": sha256_of(cu)},
     }
+    if w.history is not None:
+        cuk = torch.from_numpy(cu_seqlens_of(kv_lengths))
+        out["cu_seqlens_k"] = cuk
+        out["kv_lengths"] = kv_lengths
+        out["sha256"]["cu_seqlens_k"] = sha256_of(cuk)
+    return out
 
 
 def sample_rows(lengths: Sequence[int], n_q_heads: int, n: int, seed: int

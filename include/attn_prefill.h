@@ -116,6 +116,31 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k,
                  int32_t n_kv_heads, int32_t head_dim, float scale,
                  int32_t sliding_window, attn_stream_t stream);
 
+/* Chunked prefill against a KV history.  A later prefill chunk attends to
+ * every earlier token of its sequence, not only to the chunk (the
+ * multi-chunk fix in atlas PR #69: later chunks use kv_len =
+ * seq_len_start + n).  Sequence s has Lq = cu_seqlens_q[s+1] - cu_seqlens_q[s]
+ * new queries in q / out and Lk = cu_seqlens_k[s+1] - cu_seqlens_k[s] >= Lq
+ * keys and values in k / v: its history followed by the chunk's own tokens.
+ * The queries are the sequence's last Lq positions, so local query i has
+ * position p = Lk - Lq + i and sees the keys j <= p (and j >= p - W + 1 for
+ * a window W > 0); with Lq == Lk this is attn_prefill.
+ *   q, out: n_tokens = Tq (packed by cu_seqlens_q)
+ *   k, v:   n_tokens = Tk (packed by cu_seqlens_k); Tk = 0 with Tq > 0 is
+ *           ATTN_ERR_INVALID_ARG
+ *   cu_seqlens_q, cu_seqlens_k: device offsets with the same n_seqs
+ * Other arguments, layouts, precision, ownership and errors as for
+ * attn_prefill.  Offsets are not read by the host; the kernel clamps them
+ * into [0, Tq] and [0, Tk], and a query left without a visible key (only
+ * possible with Lq > Lk, outside the contract) gets an all-zero row.
+ * ATTN_PREFILL_VALIDATE=1 also checks Lq <= Lk per sequence. */
+int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k,
+                         const attn_tensor* v, const attn_tensor* out,
+                         const attn_seqlens* cu_seqlens_q,
+                         const attn_seqlens* cu_seqlens_k, int32_t n_q_heads,
+                         int32_t n_kv_heads, int32_t head_dim, float scale,
+                         int32_t sliding_window, attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_prefill_status_string(int status);
 

@@ -188,3 +188,71 @@ def test_binding_refuses_cpu_tensors():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError):
         B.attn_prefill(q, q, q, q.clone(), cu, 1, 1, 128, 0.1)
+
+
+# ---- attn_prefill_chunked: the same checks plus the history arguments
+
+
+def chunked_args(nq=64, nk=256, hq=32, hkv=1, d=128):
+    a = base_args(n=nq, hq=hq, hkv=hkv, d=d)
+    a["k"] = mutate(a["k"], n_tokens=nk)
+    a["v"] = mutate(a["v"], n_tokens=nk)
+    a["seqlens_k"] = B.AttnSeqlens(FAKE + (5 << 30), 1, 0)
+    return a
+
+
+def call_chunked(**kw):
+    return B.call_raw_chunked(kw["q"], kw["k"], kw["v"], kw["out"], kw["seqlens"],
+                              kw["seqlens_k"], kw["n_q_heads"], kw["n_kv_heads"],
+                              kw["head_dim"], kw["scale"], kw["sliding_window"], None)
+
+
+BAD_CHUNKED = [
+    ("out_tokens_differ_from_q", lambda a: with_(a, out=mutate(a["out"], n_tokens=63)),
+     B.ATTN_ERR_INVALID_ARG, "q 64 out 63"),
+    ("v_tokens_differ_from_k", lambda a: with_(a, v=mutate(a["v"], n_tokens=255)),
+     B.ATTN_ERR_INVALID_ARG, "k 256 v 255"),
+    ("no_keys_for_queries", lambda a: with_(a, k=mutate(a["k"], n_tokens=0, data=None),
+                                            v=mutate(a["v"], n_tokens=0, data=None)),
+     B.ATTN_ERR_INVALID_ARG, "k and v have none"),
+    ("seqlens_k_null_data", lambda a: with_(a, seqlens_k=B.AttnSeqlens(None, 1, 0)),
+     B.ATTN_ERR_INVALID_ARG, "cu_seqlens_k data"),
+    ("seqlens_k_count_differs", lambda a: with_(a, seqlens_k=B.AttnSeqlens(FAKE, 2, 0)),
+     B.ATTN_ERR_INVALID_ARG, "cu_seqlens_k 2"),
+    ("seqlens_k_negative_hint", lambda a: with_(a, seqlens_k=B.AttnSeqlens(FAKE, 1, -1)),
+     B.ATTN_ERR_INVALID_ARG, "max_seqlen"),
+    ("k_stride_beyond_buffer_range",
+     lambda a: with_(a, k=mutate(a["k"], token_stride=1 << 24)),
+     B.ATTN_ERR_UNSUPPORTED, "k: token stride"),
+    ("head_dim_64_unsupported", lambda a: with_(a, head_dim=64),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 64"),
+    ("out_aliases_v", lambda a: with_(a, out=mutate(a["out"], data=a["v"].data + 4096)),
+     B.ATTN_ERR_INVALID_ARG, "overlaps"),
+]
+
+
+@pytest.mark.parametrize("name,mut,status,frag", BAD_CHUNKED,
+                         ids=[b[0] for b in BAD_CHUNKED])
+def test_chunked_bad_argument_rejected_on_host(name, mut, status, frag):
+    rc = call_chunked(**mut(chunked_args()))
+    assert rc == status, (rc, B.last_error())
+    assert frag in B.last_error(), B.last_error()
+
+
+def test_chunked_null_key_offsets_rejected():
+    lib = B.load_library()
+    a = chunked_args()
+    rc = lib.attn_prefill_chunked(ctypes.byref(a["q"]), ctypes.byref(a["k"]),
+                                  ctypes.byref(a["v"]), ctypes.byref(a["out"]),
+                                  ctypes.byref(a["seqlens"]), None,
+                                  32, 1, 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "cu_seqlens_k is NULL" in B.last_error()
+
+
+def test_chunked_empty_queries_are_a_no_op_without_hip():
+    # no new tokens: nothing to write, even with a KV history present
+    a = chunked_args(nq=0)
+    for key in ("q", "out"):
+        a[key] = mutate(a[key], data=None)
+    assert call_chunked(**a) == B.ATTN_OK
+    assert B.last_error() == ""

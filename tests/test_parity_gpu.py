@@ -58,6 +58,8 @@ def check(name, got, want):
 
 
 def run_gpu(inp, hq, hkv, d, scale, window, out=None):
+    """One launch through the C ABI; inputs with a KV history go through
+    attn_prefill_chunked."""
     dev = torch.device("cuda:0")
     q = inp["q"].to(dev)
     k = inp["k"].to(dev)
@@ -65,9 +67,21 @@ def run_gpu(inp, hq, hkv, d, scale, window, out=None):
     cu = inp["cu_seqlens"].to(dev)
     if out is None:
         out = torch.empty(q.shape[0], hq, d, dtype=torch.bfloat16, device=dev)
-    binding.attn_prefill(q, k, v, out, cu, hq, hkv, d, scale, window)
+    if "cu_seqlens_k" in inp:
+        binding.attn_prefill_chunked(q, k, v, out, cu, inp["cu_seqlens_k"].to(dev),
+                                     hq, hkv, d, scale, window)
+    else:
+        binding.attn_prefill(q, k, v, out, cu, hq, hkv, d, scale, window)
     torch.cuda.synchronize()
     return out
+
+
+def oracle_of(inp, hq, hkv, scale, window):
+    if "cu_seqlens_k" in inp:
+        return oracle.attention_chunked(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                        inp["cu_seqlens_k"], hq, hkv, scale, window)
+    return oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                   hq, hkv, scale, window)
 
 
 def to64(t):
@@ -289,8 +303,100 @@ def test_full_size_sampled(name):
     rows = workloads.sample_rows(inp["lengths"], w.n_q_heads, 256, seed=w.seed)
     want = oracle.attention_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
                                  w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window,
-                                 rows)
+                                 rows, cu_seqlens_k=inp.get("cu_seqlens_k"))
     got = to64(out)
     got_rows = np.stack([got[t, h] for t, h in rows])
     check(f"{name}_sampled{len(rows)}", got_rows, want)
     assert np.all(np.isfinite(got)), "non-finite output somewhere"
+
+
+# ------------------------------------- chunked prefill against a KV history
+CHUNK_PAIRS = [(1, 1), (1, 200), (2, 2), (63, 64), (64, 64), (65, 300), (128, 1000),
+               (200, 200), (0, 50), (257, 258), (3, 700), (256, 256), (255, 1023),
+               (129, 129)]
+CHUNK_WINDOWS = [0, 1, 2, 63, 64, 65, 256, 1000]
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2)])
+@pytest.mark.parametrize("scale", [1 / math.sqrt(128), 1.0, -0.3])
+def test_chunked_grid_packed(hq, hkv, scale):
+    lq = [a for a, _ in CHUNK_PAIRS]
+    hist = [b - a for a, b in CHUNK_PAIRS]
+    w = workloads.custom(f"chunk_grid_h{hq}x{hkv}", lq, hq, hkv, seed=71, scale=scale,
+                         history=hist)
+    inp = workloads.make_inputs(w)
+    for win in CHUNK_WINDOWS:
+        _announce(f"{w.name} s={scale:.3f} W={win}")
+        out = run_gpu(inp, hq, hkv, 128, scale, win)
+        check(f"chunk_grid_h{hq}x{hkv}_s{scale:.3f}_w{win}", to64(out),
+              oracle_of(inp, hq, hkv, scale, win))
+
+
+@pytest.mark.parametrize("qd,kvd", [("fp32", "fp16"), ("bf16", "fp16")])
+def test_chunked_dtype_variants(qd, kvd):
+    w = workloads.custom(f"chunk_dt_{qd}_{kvd}", [190, 33, 400], 8, 2, q_dtype=qd,
+                         kv_dtype=kvd, seed=72, history=[500, 0, 129])
+    inp = workloads.make_inputs(w)
+    for win in (0, 100):
+        _announce(f"{w.name} W={win}")
+        out = run_gpu(inp, 8, 2, 128, w.attn_scale, win)
+        check(f"{w.name}_w{win}", to64(out), oracle_of(inp, 8, 2, w.attn_scale, win))
+
+
+def test_chunked_without_history_is_attn_prefill_bitwise():
+    w = workloads.custom("chunk_nohist", [700, 1, 300], 32, 1, seed=73,
+                         history=[0, 0, 0])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    a = run_gpu(inp, 32, 1, 128, w.attn_scale, 0).clone()
+    plain = {k: v for k, v in inp.items() if k != "cu_seqlens_k"}
+    b = run_gpu(plain, 32, 1, 128, w.attn_scale, 0)
+    assert torch.equal(a, b)
+
+
+def test_chunk_by_chunk_matches_single_pass():
+    """A sequence prefilled chunk by chunk against its growing KV history
+    gives the single-pass rows (the multi-chunk contract)."""
+    dev = torch.device("cuda:0")
+    n, hq = 1000, 32
+    w = workloads.custom("chunk_split", [n], hq, 1, seed=74)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    full = to64(run_gpu(inp, hq, 1, 128, w.attn_scale, 0))
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    for a, b in ((0, 300), (300, 301), (301, 777), (777, 1000)):
+        out = torch.empty(b - a, hq, 128, dtype=torch.bfloat16, device=dev)
+        cq = torch.tensor([0, b - a], dtype=torch.int32, device=dev)
+        ck = torch.tensor([0, b], dtype=torch.int32, device=dev)
+        binding.attn_prefill_chunked(q[a:b], k[:b], v[:b], out, cq, ck, hq, 1, 128,
+                                     w.attn_scale, 0)
+        torch.cuda.synchronize()
+        got = to64(out)
+        diff = float(np.max(np.abs(got - full[a:b])))
+        sys.stdout.write(f"[chunk] rows {a}..{b}: max |chunked - single pass| = {diff}\n")
+        assert diff <= 1e-2, (a, b, diff)
+        want = oracle.attention_chunked(inp["q"][a:b], inp["k"][:b], inp["v"][:b],
+                                        [0, b - a], [0, b], hq, 1, w.attn_scale, 0)
+        check(f"chunk_split_{a}_{b}", got, want)
+
+
+def test_chunked_more_queries_than_keys_is_memory_safe():
+    """Lq > Lk is outside the contract: queries left without a visible key
+    get zero rows, the others follow the definition, nothing outside `out`
+    is written."""
+    dev = torch.device("cuda:0")
+    w = workloads.custom("chunk_short_kv", [10], 4, 1, seed=75, history=[0])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    ob = torch.full((14, 4, 128), 7.0, dtype=torch.bfloat16, device=dev)
+    out = ob[2:12]
+    cq = torch.tensor([0, 10], dtype=torch.int32, device=dev)
+    ck = torch.tensor([0, 4], dtype=torch.int32, device=dev)
+    binding.attn_prefill_chunked(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+                                 out, cq, ck, 4, 1, 128, w.attn_scale, 0)
+    torch.cuda.synchronize()
+    assert torch.all(ob[:2].float() == 7.0) and torch.all(ob[12:].float() == 7.0)
+    want = oracle.attention_chunked(inp["q"], inp["k"][:4], inp["v"][:4], [0, 10],
+                                    [0, 4], 4, 1, w.attn_scale, 0)
+    assert np.all(want[:6] == 0.0)
+    check("chunk_short_kv", to64(out), want)

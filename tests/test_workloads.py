@@ -64,3 +64,36 @@ def test_sample_rows_cover_edges():
     for r in [(0, 0), (0, 3), (2, 0), (3, 0), (7, 0), (7, 3)]:
         assert r in rows
     assert all(0 <= t < 8 and 0 <= h < 4 for t, h in rows)
+
+
+@pytest.mark.parametrize("nq,nk,w", [(0, 5, 0), (1, 1, 0), (1, 9, 0), (3, 9, 0),
+                                     (9, 9, 3), (4, 20, 5), (20, 20, 0),
+                                     (7, 100, 1), (64, 200, 64), (5, 3, 0)])
+def test_history_pair_count_matches_brute_count(nq, nk, w):
+    assert (measure.visible_pairs_history(nq, nk, w)
+            == oracle.visible_pairs([nk], w, q_lengths=[nq]))
+
+
+def test_chunked_workload_shapes_and_prefix_draws():
+    w = workloads.WORKLOADS["chunks8_gqa32q8kv_history"]
+    inp = workloads.make_inputs(w)
+    tq = sum(w.lengths)
+    tk = sum(h + n for h, n in zip(w.history, w.lengths))
+    assert inp["q"].shape == (tq, 32, 128)
+    assert inp["k"].shape == (tk, 8, 128) and inp["v"].shape == (tk, 8, 128)
+    assert inp["cu_seqlens_k"].tolist()[-1] == tk
+    assert inp["kv_lengths"] == [h + n for h, n in zip(w.history, w.lengths)]
+    # without a history the draws are the plain workload's
+    plain = workloads.custom("p", [5, 7], 4, 1, seed=9)
+    hist0 = workloads.custom("p", [5, 7], 4, 1, seed=9, history=[0, 0])
+    a, b = workloads.make_inputs(plain), workloads.make_inputs(hist0)
+    assert torch.equal(a["q"], b["q"]) and torch.equal(a["k"], b["k"])
+    assert b["cu_seqlens_k"].tolist() == a["cu_seqlens"].tolist()
+
+
+def test_chunked_headline_shape_flops():
+    w = workloads.WORKLOADS["chunk2048_hist6144_32q1kv_outliers"]
+    f = measure.causal_flops(list(w.lengths), w.n_q_heads, w.head_dim, w.window,
+                             kv_lengths=[8192])
+    # positions 6144..8191 see p + 1 keys each
+    assert f == 4 * 128 * 32 * sum(p + 1 for p in range(6144, 8192))
