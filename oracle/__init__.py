@@ -6,8 +6,10 @@ leg of ``bench.py``; never by the library or its binding.
 from .attention import (  # noqa: F401
     attention_chunked,
     attention_head,
+    attention_paged,
     attention_rows,
     attention_varlen,
+    gather_pages,
     kv_head_of,
     softmax_probs,
     visibility,

@@ -38,6 +38,14 @@ visibility rule of step 3 is applied to that position.  With ``Lq == Lk``
 this is exactly the definition above.  A query with no visible key (only
 possible when ``Lq > Lk``, outside the contract) has an all-zero output row.
 
+Paged KV (``attention_paged``): the keys and values live in page pools of
+``page_size`` token slots per page (the paged MLA prefill of atlas PR #69
+reads every key through a page-table lookup; the m40-llm AGENTS.md page
+addresses the cache per [sequence][position][kv_head][head_dim]).  Key
+position ``j`` of sequence ``s`` is slot ``j % page_size`` of page
+``block_table[s][j // page_size]``; ``seqlens_k[s]`` gives ``Lk``.  The result
+is ``attention_chunked`` on the keys and values gathered in position order.
+
 The online-softmax recurrence that the GPU kernel uses (the fused MLA prefill
 commit on the atlas PR #69 page) is a reordering of steps 4-5 and is not
 used here.  The head grouping ``g = h // group`` is the consecutive GQA
@@ -59,6 +67,8 @@ __all__ = [
     "attention_head",
     "attention_varlen",
     "attention_chunked",
+    "attention_paged",
+    "gather_pages",
     "attention_rows",
     "visible_pairs",
 ]
@@ -220,6 +230,39 @@ def attention_chunked(q, k, v, cu_seqlens_q, cu_seqlens_k, n_q_heads: int,
             for f in [pool.submit(run, job) for job in jobs]:
                 f.result()
     return out
+
+
+def gather_pages(pool, block_table, seqlens_k, page_size: int):
+    """Keys (or values) of every sequence in position order, packed.
+
+    ``pool``: ``[n_pages * page_size, heads, d]`` token slots;
+    ``block_table``: ``[n_seqs, table_width]`` physical page numbers;
+    ``seqlens_k``: keys per sequence.  Returns the packed float64 tensor and
+    its ``n_seqs + 1`` offsets.
+    """
+    pool = _as_f64(pool)
+    table = np.asarray(_as_f64(block_table), dtype=np.int64)
+    lens = [int(x) for x in np.asarray(_as_f64(seqlens_k)).reshape(-1)]
+    parts, cu = [], [0]
+    for s, n in enumerate(lens):
+        pos = np.arange(n)
+        slots = table[s, pos // page_size] * page_size + pos % page_size
+        parts.append(pool[slots])
+        cu.append(cu[-1] + n)
+    packed = (np.concatenate(parts) if parts else
+              np.zeros((0,) + pool.shape[1:], dtype=np.float64))
+    return packed, cu
+
+
+def attention_paged(q, k_pool, v_pool, cu_seqlens_q, block_table, seqlens_k,
+                    page_size: int, n_q_heads: int, n_kv_heads: int,
+                    scale: float, window: int,
+                    workers: Optional[int] = None) -> np.ndarray:
+    """Chunked prefill whose KV history is read through a block table."""
+    k, cu_k = gather_pages(k_pool, block_table, seqlens_k, page_size)
+    v, _ = gather_pages(v_pool, block_table, seqlens_k, page_size)
+    return attention_chunked(q, k, v, cu_seqlens_q, cu_k, n_q_heads, n_kv_heads,
+                             scale, window, workers=workers)
 
 
 def attention_rows(q, k, v, cu_seqlens, n_q_heads: int, n_kv_heads: int,

@@ -86,3 +86,42 @@ def brute_attention_chunked(q, k, v, cu_q, cu_k, n_q_heads, n_kv_heads, scale,
                         acc += wgt * v[ka + j][g][c]
                     out[t][h][c] = acc / z
     return out
+
+
+def brute_attention_paged(q, k_pool, v_pool, cu_q, block_table, seqlens_k,
+                          page_size, n_q_heads, n_kv_heads, scale, window):
+    """Paged KV, literal loops: key position j of sequence s is read from
+    slot j % page_size of page block_table[s][j // page_size]."""
+    total = len(q)
+    d_v = len(v_pool[0][0]) if len(v_pool) else 0
+    out = [[[0.0] * d_v for _ in range(n_q_heads)] for _ in range(total)]
+    for s in range(len(cu_q) - 1):
+        qa, qb = cu_q[s], cu_q[s + 1]
+        n_k = seqlens_k[s]
+
+        def slot(j):
+            return block_table[s][j // page_size] * page_size + j % page_size
+
+        for t in range(qa, qb):
+            pos = n_k - (qb - qa) + (t - qa)
+            for h in range(n_q_heads):
+                g = (h * n_kv_heads) // n_q_heads
+                keys = [j for j in range(n_k)
+                        if j <= pos and not (window and pos - j >= window)]
+                if not keys:
+                    continue
+                scores = []
+                for j in keys:
+                    acc = 0.0
+                    for c in range(len(q[t][h])):
+                        acc += q[t][h][c] * k_pool[slot(j)][g][c]
+                    scores.append(scale * acc)
+                top = max(scores)
+                weights = [math.exp(x - top) for x in scores]
+                z = sum(weights)
+                for c in range(d_v):
+                    acc = 0.0
+                    for wgt, j in zip(weights, keys):
+                        acc += wgt * v_pool[slot(j)][g][c]
+                    out[t][h][c] = acc / z
+    return out

@@ -134,6 +134,39 @@ EXAMPLES += [
         [[[0.75]], [[2.0]]]),
 ]
 
+# Paged KV: key position j of sequence s is slot j % page_size of page
+# block_table[s][j // page_size] (atlas PR #69, paged MLA prefill: a page
+# table lookup per position).
+
+
+def exp_(name, why, cu_q, table, seqlens_k, page_size, hq, hkv, scale, window,
+         q, k_pool, v_pool, out):
+    e = ex(name, why, cu_q, hq, hkv, scale, window, q, k_pool, v_pool, out)
+    e.update(block_table=table, seqlens_k=seqlens_k, page_size=page_size)
+    return e
+
+
+EXAMPLES += [
+    exp_("paged_reversed_pages",
+         "page_size 1, table [2,1,0]: the pool holds the keys in reverse "
+         "order, so positions 0,1,2 read slots 2,1,0 -> the same scores "
+         "[7, 0, ln2] and values [10, 20, 50] as history2_one_query -> "
+         "(10 e^7 + 120)/(e^7 + 3)",
+         [0, 1], [[2, 1, 0]], [3], 1, 1, 1, 1.0, 0,
+         [[[1.0]]], [[[LN2]], [[0.0]], [[7.0]]],
+         [[[50.0]], [[20.0]], [[10.0]]],
+         [[[(10 * E7 + 120) / (E7 + 3)]]]),
+    exp_("paged_two_slot_pages_window2",
+         "page_size 2, table [[1, 0]] over a 4-slot pool: positions 0,1 are "
+         "slots 2,3 and position 2 is slot 0; the query at position 2 with "
+         "W=2 sees positions {1,2} = slots {3,0}, scores [0, ln2] -> "
+         "(20 + 2*50)/3 = 40",
+         [0, 1], [[1, 0]], [3], 2, 1, 1, 1.0, 2,
+         [[[1.0]]], [[[LN2]], [[-9.0]], [[7.0]], [[0.0]]],
+         [[[50.0]], [[-1.0]], [[10.0]], [[20.0]]],
+         [[[40.0]]]),
+]
+
 if __name__ == "__main__":
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "worked_examples.json")

@@ -14,7 +14,10 @@ disagrees with:
   rendering of the causal case,
 * for chunked prefill against a KV history: the literal-loop brute force,
   and the fact that running a sequence chunk by chunk against its growing
-  history reproduces the single-pass rows.
+  history reproduces the single-pass rows,
+* for a paged KV cache: a literal-loop brute force that addresses every key
+  through the block table itself, and invariance under a permutation of the
+  physical pages.
 """
 from __future__ import annotations
 
@@ -24,7 +27,8 @@ import os
 
 import numpy as np
 
-from bruteforce import brute_attention, brute_attention_chunked
+from bruteforce import (brute_attention, brute_attention_chunked,
+                        brute_attention_paged)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                       "worked_examples.json")
@@ -47,7 +51,14 @@ def pin_golden(mod):
     with open(GOLDEN) as f:
         examples = json.load(f)["examples"]
     for ex in examples:
-        if "cu_seqlens_k" in ex:
+        if "block_table" in ex:
+            got = mod.attention_paged(np.array(ex["q"]), np.array(ex["k"]),
+                                      np.array(ex["v"]), ex["cu_seqlens"],
+                                      np.array(ex["block_table"]), ex["seqlens_k"],
+                                      ex["page_size"], ex["n_q_heads"],
+                                      ex["n_kv_heads"], ex["scale"], ex["window"],
+                                      workers=1)
+        elif "cu_seqlens_k" in ex:
             got = mod.attention_chunked(np.array(ex["q"]), np.array(ex["k"]),
                                         np.array(ex["v"]), ex["cu_seqlens"],
                                         ex["cu_seqlens_k"], ex["n_q_heads"],
@@ -298,6 +309,64 @@ def pin_chunks_reproduce_single_pass(mod):
         assert np.max(np.abs(got - full)) <= 1e-12, w
 
 
+PAGED_CASES = [
+    # q lengths, kv lengths, page_size, hq, hkv, d, window, scale
+    ([1], [5], 2, 1, 1, 2, 0, 0.8),
+    ([3, 2], [7, 2], 4, 2, 1, 3, 0, 0.6),
+    ([4, 0, 6], [9, 3, 6], 3, 4, 2, 2, 2, -0.5),
+    ([8], [8], 8, 2, 2, 2, 3, 1.2),
+]
+
+
+def _paged_case(rng, lq, lk, page, hq, hkv, d):
+    n_pages = sum((n + page - 1) // page for n in lk) + 3  # spare pages
+    width = max(1, max((n + page - 1) // page for n in lk))
+    perm = rng.permutation(n_pages)
+    table = np.zeros((len(lk), width), dtype=np.int64)
+    used = 0
+    for s, n in enumerate(lk):
+        for b in range((n + page - 1) // page):
+            table[s, b] = perm[used]
+            used += 1
+    q = rng.standard_normal((sum(lq), hq, d))
+    kp = rng.standard_normal((n_pages * page, hkv, d))
+    vp = rng.standard_normal((n_pages * page, hkv, d))
+    return q, kp, vp, table
+
+
+def pin_paged_bruteforce(mod):
+    for case_id, (lq, lk, page, hq, hkv, d, w, scale) in enumerate(PAGED_CASES):
+        rng = np.random.default_rng(400 + case_id)
+        q, kp, vp, table = _paged_case(rng, lq, lk, page, hq, hkv, d)
+        cq = _cu(lq)
+        want = np.array(brute_attention_paged(
+            q.tolist(), kp.tolist(), vp.tolist(), cq, table.tolist(), lk, page, hq,
+            hkv, scale, w)).reshape(q.shape[0], hq, d)
+        got = mod.attention_paged(q, kp, vp, cq, table, lk, page, hq, hkv, scale, w,
+                                  workers=1)
+        err = np.max(np.abs(got - want)) if got.size else 0.0
+        assert err <= 1e-12, f"paged case {case_id}: max err {err}"
+
+
+def pin_paged_page_permutation_invariance(mod):
+    # moving the pages and rewriting the table to match changes nothing
+    rng = np.random.default_rng(41)
+    lq, lk, page, hq, hkv, d = [5, 9], [13, 9], 4, 4, 2, 8
+    q, kp, vp, table = _paged_case(rng, lq, lk, page, hq, hkv, d)
+    a = mod.attention_paged(q, kp, vp, _cu(lq), table, lk, page, hq, hkv, 0.4, 0,
+                            workers=1)
+    n_pages = kp.shape[0] // page
+    perm = rng.permutation(n_pages)  # new page of old page p is perm[p]
+    kp2 = np.zeros_like(kp)
+    vp2 = np.zeros_like(vp)
+    for old in range(n_pages):
+        kp2[perm[old] * page:(perm[old] + 1) * page] = kp[old * page:(old + 1) * page]
+        vp2[perm[old] * page:(perm[old] + 1) * page] = vp[old * page:(old + 1) * page]
+    b = mod.attention_paged(q, kp2, vp2, _cu(lq), perm[table], lk, page, hq, hkv,
+                            0.4, 0, workers=1)
+    assert np.max(np.abs(a - b)) <= 1e-12
+
+
 ALL_PINS = [
     pin_golden,
     pin_bruteforce,
@@ -314,4 +383,6 @@ ALL_PINS = [
     pin_parallel_equals_serial,
     pin_chunked_bruteforce,
     pin_chunks_reproduce_single_pass,
+    pin_paged_bruteforce,
+    pin_paged_page_permutation_invariance,
 ]

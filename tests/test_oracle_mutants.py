@@ -116,6 +116,37 @@ def _chunk_keys_only(mod):
     return attention_chunked
 
 
+def _paged_wrong_slot(mod):
+    # reads key j from the page of logical block j // page_size but ignores
+    # the table (physical page = logical page of sequence 0)
+    def gather_pages(pool, block_table, seqlens_k, page_size):
+        pool = np.asarray(pool, dtype=np.float64)
+        lens = [int(x) for x in np.asarray(seqlens_k).reshape(-1)]
+        parts, cu = [], [0]
+        for s, n in enumerate(lens):
+            parts.append(pool[np.arange(n)])
+            cu.append(cu[-1] + n)
+        return np.concatenate(parts), cu
+    return gather_pages
+
+
+def _paged_slot_transposed(mod):
+    # swaps the roles of page and slot: page j % page_size, slot j // page_size
+    def gather_pages(pool, block_table, seqlens_k, page_size):
+        pool = np.asarray(pool, dtype=np.float64)
+        table = np.asarray(block_table, dtype=np.int64)
+        lens = [int(x) for x in np.asarray(seqlens_k).reshape(-1)]
+        parts, cu = [], [0]
+        for s, n in enumerate(lens):
+            pos = np.arange(n)
+            blk = np.minimum(pos % page_size, table.shape[1] - 1)
+            slots = table[s, blk] * page_size + np.minimum(pos // page_size, page_size - 1)
+            parts.append(pool[slots])
+            cu.append(cu[-1] + n)
+        return np.concatenate(parts), cu
+    return gather_pages
+
+
 MUTANTS = {
     "causal_excludes_self": ("visibility", _vis(
         lambda i, j, w: (j < i) | ((i == 0) & (j == 0)) if w == 0 else
@@ -139,6 +170,8 @@ MUTANTS = {
     "history_ignored": ("softmax_probs", _probs("history_ignored")),
     "history_offset_plus_one": ("softmax_probs", _probs("history_offset_plus_one")),
     "chunk_sees_only_its_own_keys": ("attention_chunked", None),
+    "paged_table_ignored": ("gather_pages", None),
+    "paged_page_and_slot_swapped": ("gather_pages", None),
 }
 
 
@@ -154,5 +187,9 @@ def test_mutant_is_caught(name):
         repl = _no_isolation(mod)
     if name == "chunk_sees_only_its_own_keys":
         repl = _chunk_keys_only(mod)
+    if name == "paged_table_ignored":
+        repl = _paged_wrong_slot(mod)
+    if name == "paged_page_and_slot_swapped":
+        repl = _paged_slot_transposed(mod)
     setattr(mod, attr, repl)
     assert failing_pins(mod), f"mutant {name} passed every pin"
