@@ -23,7 +23,8 @@ ATTN_FP16 = 1
 ATTN_FP32 = 2
 
 #: Every symbol include/attn_prefill.h declares.
-EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_status_string",
+EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_paged",
+           "attn_prefill_status_string",
            "attn_prefill_last_error", "attn_prefill_supported_head_dims",
            "attn_prefill_version")
 
@@ -37,6 +38,11 @@ class AttnTensor(ctypes.Structure):
 class AttnSeqlens(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("n_seqs", ctypes.c_int32),
                 ("max_seqlen", ctypes.c_int32)]
+
+
+class AttnPagedKV(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("seqlens_k", ctypes.c_void_p),
+                ("table_stride", ctypes.c_int32), ("page_size", ctypes.c_int32)]
 
 
 class AttnPrefillError(RuntimeError):
@@ -71,6 +77,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
         ctypes.POINTER(AttnSeqlens), ctypes.POINTER(AttnSeqlens), ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_prefill_paged.restype = ctypes.c_int
+    lib.attn_prefill_paged.argtypes = [
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnSeqlens), ctypes.POINTER(AttnPagedKV), ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
     lib.attn_prefill_status_string.restype = ctypes.c_char_p
     lib.attn_prefill_status_string.argtypes = [ctypes.c_int]
@@ -121,6 +133,18 @@ def call_raw_chunked(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTenso
         ctypes.byref(seqlens_q), ctypes.byref(seqlens_k), int(n_q_heads),
         int(n_kv_heads), int(head_dim), float(scale), int(sliding_window),
         ctypes.c_void_p(stream))
+
+
+def call_raw_paged(q: AttnTensor, k_pool: AttnTensor, v_pool: AttnTensor,
+                   out: AttnTensor, seqlens_q: AttnSeqlens, paged: AttnPagedKV,
+                   n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
+                   sliding_window: int, stream: Optional[int] = None) -> int:
+    """Calls ``attn_prefill_paged`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_prefill_paged(
+        ctypes.byref(q), ctypes.byref(k_pool), ctypes.byref(v_pool), ctypes.byref(out),
+        ctypes.byref(seqlens_q), ctypes.byref(paged), int(n_q_heads), int(n_kv_heads),
+        int(head_dim), float(scale), int(sliding_window), ctypes.c_void_p(stream))
 
 
 def _dtype_code(t) -> int:
@@ -178,6 +202,34 @@ def attn_prefill_chunked(q, k, v, out, cu_seqlens_q, cu_seqlens_k, n_q_heads: in
     status = call_raw_chunked(describe(q), describe(k), describe(v), describe(out),
                               sq, sk, n_q_heads, n_kv_heads, head_dim, scale,
                               sliding_window, _stream_handle(q, stream))
+    if status != ATTN_OK:
+        raise AttnPrefillError(status, last_error())
+
+
+def attn_prefill_paged(q, k_pool, v_pool, out, cu_seqlens_q, block_table, seqlens_k,
+                       page_size: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                       scale: float, sliding_window: int = 0, stream=None) -> None:
+    """Chunked prefill against a paged K/V cache; ``out`` is written in place.
+
+    k_pool, v_pool: [n_pages * page_size, n_kv_heads, head_dim] token slots;
+    block_table: int32 GPU tensor [n_seqs, table_stride] of page numbers;
+    seqlens_k: int32 GPU tensor [n_seqs] of keys per sequence.
+    """
+    import torch
+
+    sq = _seqlens(cu_seqlens_q, "cu_seqlens_q")
+    for t, name in ((block_table, "block_table"), (seqlens_k, "seqlens_k")):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if block_table.dim() != 2 or seqlens_k.dim() != 1:
+        raise ValueError("block_table must be [n_seqs, width], seqlens_k [n_seqs]")
+    if block_table.shape[0] != sq.n_seqs or seqlens_k.shape[0] != sq.n_seqs:
+        raise ValueError("block_table / seqlens_k rows must match the sequences")
+    pg = AttnPagedKV(block_table.data_ptr(), seqlens_k.data_ptr(),
+                     block_table.shape[1], page_size)
+    status = call_raw_paged(describe(q), describe(k_pool), describe(v_pool), describe(out),
+                            sq, pg, n_q_heads, n_kv_heads, head_dim, scale,
+                            sliding_window, _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
 

@@ -143,12 +143,49 @@ int check_seqlens(const attn_seqlens* cu, const char* what) {
   return ATTN_OK;
 }
 
-// Both entry points: cu_k == nullptr means the keys are the queries' own
-// tokens (no history).
+// Debug-only host check of a paged cache's device metadata.
+int debug_validate_paged(const attn_seqlens* cu_q, int64_t n_q, const attn_paged_kv* pg,
+                         int64_t n_pages, hipStream_t stream) {
+  std::vector<int32_t> hq;
+  int rc;
+  if ((rc = read_offsets(cu_q, hq, stream, "cu_seqlens")) != ATTN_OK) return rc;
+  if ((rc = check_offsets(hq, n_q, "cu_seqlens")) != ATTN_OK) return rc;
+  const size_t n_seqs = hq.size() - 1;
+  std::vector<int32_t> lens(n_seqs), table(n_seqs * (size_t)pg->table_stride);
+  hipError_t e = hipMemcpy(lens.data(), pg->seqlens_k, lens.size() * sizeof(int32_t),
+                           hipMemcpyDeviceToHost);
+  if (e == hipSuccess)
+    e = hipMemcpy(table.data(), pg->block_table, table.size() * sizeof(int32_t),
+                  hipMemcpyDeviceToHost);
+  if (e != hipSuccess)
+    return fail(ATTN_ERR_HIP, "ATTN_PREFILL_VALIDATE: reading the paged metadata failed: %s",
+                hipGetErrorString(e));
+  const int64_t cap = (int64_t)pg->table_stride * pg->page_size;
+  for (size_t s = 0; s < n_seqs; ++s) {
+    if (lens[s] < 0 || lens[s] > cap)
+      return fail(ATTN_ERR_INVALID_ARG, "seqlens_k[%zu] = %d outside [0, %lld]", s, lens[s],
+                  (long long)cap);
+    if (hq[s + 1] - hq[s] > lens[s])
+      return fail(ATTN_ERR_INVALID_ARG, "sequence %zu has %d queries but only %d keys", s,
+                  hq[s + 1] - hq[s], lens[s]);
+    const int used = (lens[s] + pg->page_size - 1) / pg->page_size;
+    for (int b = 0; b < used; ++b) {
+      const int32_t page = table[s * (size_t)pg->table_stride + b];
+      if (page < 0 || page >= n_pages)
+        return fail(ATTN_ERR_INVALID_ARG, "block_table[%zu][%d] = %d outside [0, %lld)", s, b,
+                    page, (long long)n_pages);
+    }
+  }
+  return ATTN_OK;
+}
+
+// All entry points: cu_k == nullptr and paged == nullptr means the keys are
+// the queries' own tokens (no history); cu_k gives packed keys with a
+// history; paged gives keys in a paged cache.
 int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                 const attn_tensor* out, const attn_seqlens* cu_q, const attn_seqlens* cu_k,
-                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
-                int32_t sliding_window, attn_stream_t stream) {
+                const attn_paged_kv* paged, int32_t n_q_heads, int32_t n_kv_heads,
+                int32_t head_dim, float scale, int32_t sliding_window, attn_stream_t stream) {
   g_last_error.clear();
   if (n_q_heads < 1 || n_kv_heads < 1)
     return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
@@ -176,7 +213,7 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
   if (out->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "out dtype must be BF16");
   const int64_t T = q->n_tokens;
   const int64_t Tk = k->n_tokens;
-  if (cu_k == nullptr) {
+  if (cu_k == nullptr && paged == nullptr) {
     if (k->n_tokens != T || v->n_tokens != T || out->n_tokens != T)
       return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: q %lld k %lld v %lld out %lld",
                   (long long)T, (long long)k->n_tokens, (long long)v->n_tokens,
@@ -190,6 +227,28 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
                   (long long)v->n_tokens);
   }
   if ((rc = check_seqlens(cu_q, "cu_seqlens")) != ATTN_OK) return rc;
+  int64_t n_pages = 0;
+  if (paged != nullptr) {
+    if (paged->block_table == nullptr || paged->seqlens_k == nullptr)
+      return fail(ATTN_ERR_INVALID_ARG, "paged: block_table and seqlens_k must be set");
+    if (paged->table_stride < 1)
+      return fail(ATTN_ERR_INVALID_ARG, "paged: table_stride %d < 1", (int)paged->table_stride);
+    if (paged->page_size < 1)
+      return fail(ATTN_ERR_INVALID_ARG, "paged: page_size %d < 1", (int)paged->page_size);
+    const int tile = attnp::prefill_kv_tile(head_dim);
+    if (paged->page_size % tile != 0)
+      return fail(ATTN_ERR_UNSUPPORTED, "paged: page_size %d is not a multiple of %d",
+                  (int)paged->page_size, tile);
+    if ((int64_t)paged->table_stride * paged->page_size > INT32_MAX)
+      return fail(ATTN_ERR_UNSUPPORTED, "paged: table_stride * page_size exceeds int32");
+    if (Tk % paged->page_size != 0)
+      return fail(ATTN_ERR_INVALID_ARG, "paged: k has %lld token slots, not a multiple of "
+                  "page_size %d", (long long)Tk, (int)paged->page_size);
+    n_pages = Tk / paged->page_size;
+    if (T > 0 && n_pages == 0)
+      return fail(ATTN_ERR_INVALID_ARG, "q has %lld tokens but k and v have none",
+                  (long long)T);
+  }
   if (cu_k != nullptr) {
     if ((rc = check_seqlens(cu_k, "cu_seqlens_k")) != ATTN_OK) return rc;
     if (cu_k->n_seqs != cu_q->n_seqs)
@@ -223,9 +282,10 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
 
   const char* dbg = getenv("ATTN_PREFILL_VALIDATE");
   if (dbg != nullptr && dbg[0] == '1') {
-    if ((rc = debug_validate_offsets(cu_q, T, cu_k, Tk, reinterpret_cast<hipStream_t>(stream))) !=
-        ATTN_OK)
-      return rc;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    rc = paged != nullptr ? debug_validate_paged(cu_q, T, paged, n_pages, st)
+                          : debug_validate_offsets(cu_q, T, cu_k, Tk, st);
+    if (rc != ATTN_OK) return rc;
   }
 
   attnp::PrefillParams p;
@@ -250,6 +310,11 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
   p.group = n_q_heads / n_kv_heads;
   p.window = sliding_window;
   p.tile_slots = 0;  // set by the launcher
+  p.block_table = paged != nullptr ? paged->block_table : nullptr;
+  p.seqlens_k = paged != nullptr ? paged->seqlens_k : nullptr;
+  p.table_stride = paged != nullptr ? paged->table_stride : 0;
+  p.page_size = paged != nullptr ? paged->page_size : 0;
+  p.n_pages = (int32_t)n_pages;
   const float log2e = 1.4426950408889634f;
   if (scale == 0.f) {
     p.score_mult = 1.f;  // Q is zeroed, every visible score is 0
@@ -274,8 +339,8 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
                  const attn_tensor* out, const attn_seqlens* cu_seqlens,
                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
                  int32_t sliding_window, attn_stream_t stream) {
-  return run_prefill(q, k, v, out, cu_seqlens, nullptr, n_q_heads, n_kv_heads, head_dim, scale,
-                     sliding_window, stream);
+  return run_prefill(q, k, v, out, cu_seqlens, nullptr, nullptr, n_q_heads, n_kv_heads,
+                     head_dim, scale, sliding_window, stream);
 }
 
 int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
@@ -287,8 +352,21 @@ int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k, const attn_
     g_last_error.clear();
     return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
   }
-  return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, n_q_heads, n_kv_heads, head_dim,
-                     scale, sliding_window, stream);
+  return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, nullptr, n_q_heads, n_kv_heads,
+                     head_dim, scale, sliding_window, stream);
+}
+
+int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
+                       const attn_tensor* v_pool, const attn_tensor* out,
+                       const attn_seqlens* cu_seqlens_q, const attn_paged_kv* paged,
+                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                       int32_t sliding_window, attn_stream_t stream) {
+  if (paged == nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "paged is NULL");
+  }
+  return run_prefill(q, k_pool, v_pool, out, cu_seqlens_q, nullptr, paged, n_q_heads,
+                     n_kv_heads, head_dim, scale, sliding_window, stream);
 }
 
 const char* attn_prefill_status_string(int status) {

@@ -158,17 +158,19 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 struct Work {
   int start;   // first query token of the sequence in the packed q / out
   int len;     // number of queries (new tokens) of the sequence
-  int kstart;  // first key token of the sequence in the packed k / v
+  int kstart;  // first key token of the sequence in the packed k / v (unpaged)
   int klen;    // number of keys: the history followed by the new tokens
   int q0;      // first local query row of this tile
+  int seq;     // sequence index (the block-table row of a paged cache)
   bool valid;
 };
 
 // Maps a q-tile slot to (sequence, tile).  Slots enumerate sequences in
 // order; inside a sequence the last (most expensive causal) tile comes
 // first.  Query and key offsets are clamped into [0, T].  Every lane of the
-// wave computes the same answer.
-template <int BM>
+// wave computes the same answer.  With a paged cache the key count comes
+// from seqlens_k, clamped to the table row's capacity.
+template <int BM, bool PAGED>
 __device__ Work decode_work(const PrefillParams& p, int slot) {
   const int lane = threadIdx.x & (kWave - 1);
   int base = 0;
@@ -178,8 +180,12 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
     if (s < p.n_seqs) {
       a = min(max(p.cu_seqlens[s], 0), p.n_tokens);
       b = min(max(p.cu_seqlens[s + 1], 0), p.n_tokens);
-      ka = min(max(p.cu_seqlens_k[s], 0), p.n_tokens_k);
-      kb = min(max(p.cu_seqlens_k[s + 1], 0), p.n_tokens_k);
+      if (PAGED) {
+        kb = min(max(p.seqlens_k[s], 0), p.table_stride * p.page_size);
+      } else {
+        ka = min(max(p.cu_seqlens_k[s], 0), p.n_tokens_k);
+        kb = min(max(p.cu_seqlens_k[s + 1], 0), p.n_tokens_k);
+      }
     }
     const int len = max(b - a, 0);
     const int nt = (len + BM - 1) / BM;
@@ -202,17 +208,18 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
       const int ntiles = __shfl(nt, src, kWave);
       const int rank = slot - base - excl;  // 0 = heaviest tile
       w.q0 = (ntiles - 1 - rank) * BM;
+      w.seq = s0 + src;
       w.valid = true;
       return w;
     }
     base += total;
   }
-  Work w{0, 0, 0, 0, 0, false};
+  Work w{0, 0, 0, 0, 0, 0, false};
   return w;
 }
 
 // ------------------------------------------------------------------ kernel
-template <int HDIM, class QT, class KVT>
+template <int HDIM, class QT, class KVT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams p) {
   using C = Cfg<HDIM>;
   typedef typename QT::T qelem;
@@ -228,12 +235,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int group = wave >> 2;                                   // 0 = A, 1 = B
   const int slot = blockIdx.x / p.n_q_heads;
   const int head = blockIdx.x - slot * p.n_q_heads;
-  Work w = decode_work<kBM>(p, slot);
+  Work w = decode_work<kBM, PAGED>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
   w.start = __builtin_amdgcn_readfirstlane(w.start);
   w.len = __builtin_amdgcn_readfirstlane(w.len);
   w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
   w.kstart = __builtin_amdgcn_readfirstlane(w.kstart);
+  w.seq = __builtin_amdgcn_readfirstlane(w.seq);
   w.klen = __builtin_amdgcn_readfirstlane(w.klen);
 
   const int kvh = head / p.group;
@@ -286,6 +294,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
                        (int64_t)kvh * p.k_hs;
   const kvelem* vseq = static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts +
                        (int64_t)kvh * p.v_hs;
+  // Token slot of key position kv0 (a tile start, a multiple of kBN): packed
+  // keys are contiguous; in a paged cache the whole tile sits in the page
+  // that the block table names (page_size is a multiple of kBN), one scalar
+  // table read per tile, the page number clamped into the pool.
+  auto tile_slot = [&](int kv0) -> int64_t {
+    if (!PAGED) return kv0;
+    const int* row = p.block_table + (int64_t)w.seq * p.table_stride;
+    const int idx = __builtin_amdgcn_readfirstlane(kv0 / p.page_size);
+    const int page = min(max(row[idx], 0), p.n_pages - 1);
+    return (int64_t)page * p.page_size + (kv0 - idx * p.page_size);
+  };
   const int k_row_bytes = (int)(p.k_ts * (int64_t)sizeof(kvelem));
   const int v_row_bytes = (int)(p.v_ts * (int64_t)sizeof(kvelem));
 
@@ -300,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   };
   auto gload_k = [&](int kv0) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<kvelem*>(kseq + (int64_t)kv0 * p.k_ts), 0, rows_of(kv0) * k_row_bytes,
+        const_cast<kvelem*>(kseq + tile_slot(kv0) * p.k_ts), 0, rows_of(kv0) * k_row_bytes,
         kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
@@ -311,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   };
   auto gload_v = [&](int kv0) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<kvelem*>(vseq + (int64_t)kv0 * p.v_ts), 0, rows_of(kv0) * v_row_bytes,
+        const_cast<kvelem*>(vseq + tile_slot(kv0) * p.v_ts), 0, rows_of(kv0) * v_row_bytes,
         kRsrcWord3);
 #pragma unroll
     for (int u = 0; u < C::V_UNITS; ++u) {
@@ -623,14 +642,20 @@ hipError_t launch_one(PrefillParams p, hipStream_t stream) {
   const int64_t slots = (p.n_tokens + kBM - 1) / kBM + p.n_seqs;
   p.tile_slots = (int32_t)slots;
   const uint64_t blocks = (uint64_t)slots * (uint64_t)p.n_q_heads;
-  hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT>), dim3((uint32_t)blocks),
-                     dim3(kThreads), 0, stream, p);
+  if (p.page_size > 0)
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, true>), dim3((uint32_t)blocks),
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, false>), dim3((uint32_t)blocks),
+                       dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int prefill_min_block_m(int /*head_dim*/) { return kBM; }
+
+int prefill_kv_tile(int /*head_dim*/) { return kBN; }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
                           DType kv_dtype, hipStream_t stream) {

@@ -31,11 +31,22 @@ struct PrefillParams {
   int32_t tile_slots;         // q-tile slots in the grid (set by the launcher)
   float score_mult;           // log2(e) * |scale|, or 1 when scale == 0
   float q_mult;               // +1, -1 or 0: sign of scale folded into Q
+  // Paged K/V (page_size > 0): k and v are pools of n_pages * page_size token
+  // slots; key position j of sequence s is slot j % page_size of page
+  // block_table[s * table_stride + j / page_size]; seqlens_k[s] keys.
+  const int32_t* block_table;
+  const int32_t* seqlens_k;
+  int32_t table_stride;
+  int32_t page_size;          // 0 = packed K/V (cu_seqlens_k)
+  int32_t n_pages;
 };
 
 // Smallest number of query rows per workgroup any launch uses (the grid has
 // at most ceil(T / this) + n_seqs tile slots per query head).
 int prefill_min_block_m(int head_dim);
+
+// Keys per K/V tile; a paged cache's page_size must be a multiple of it.
+int prefill_kv_tile(int head_dim);
 
 // Launches the kernel for (head_dim, q dtype, kv dtype) on `stream`; picks
 // the workgroup size and sets p.tile_slots.  Returns hipErrorInvalidValue if

@@ -141,6 +141,40 @@ int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k,
                          int32_t n_kv_heads, int32_t head_dim, float scale,
                          int32_t sliding_window, attn_stream_t stream);
 
+/* A paged K/V cache.  k and v are pools of token slots, n_tokens =
+ * n_pages * page_size, page p holding slots [p * page_size, (p+1) *
+ * page_size) of the usual [n_tokens, n_kv_heads, head_dim] descriptor.  Key
+ * position j of sequence s is slot j % page_size of page
+ * block_table[s * table_stride + j / page_size] (the paged MLA prefill in
+ * atlas PR #69 reads every key through a page-table lookup; m40-llm
+ * AGENTS.md, "Current Progress", addresses the cache per sequence and
+ * position). */
+typedef struct {
+  const int32_t* block_table;  /* DEVICE int32[n_seqs * table_stride]: pages */
+  const int32_t* seqlens_k;    /* DEVICE int32[n_seqs]: keys per sequence
+                                  (history + the chunk's own tokens)       */
+  int32_t table_stride;        /* entries per sequence row, >= 1           */
+  int32_t page_size;           /* slots per page: a multiple of 64         */
+} attn_paged_kv;
+
+/* Chunked prefill whose keys and values are read from a paged cache: as
+ * attn_prefill_chunked with sequence s's Lk = seqlens_k[s] keys at the
+ * positions the block table maps (the chunk's own K/V must already be in
+ * the cache).  q and out are packed by cu_seqlens_q; k_pool and v_pool are
+ * the pools above (same dtype, same n_tokens).  page_size not a multiple
+ * of 64 is ATTN_ERR_UNSUPPORTED; n_tokens not a multiple of page_size, an
+ * empty pool with Tq > 0, table_stride < 1 or a NULL table pointer is
+ * ATTN_ERR_INVALID_ARG.  The device metadata is not read by the host: the
+ * kernel clamps seqlens_k into [0, table_stride * page_size] and every page
+ * number into [0, n_pages), so bad metadata gives wrong output but stays in
+ * bounds; ATTN_PREFILL_VALIDATE=1 checks it on the host. */
+int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
+                       const attn_tensor* v_pool, const attn_tensor* out,
+                       const attn_seqlens* cu_seqlens_q,
+                       const attn_paged_kv* paged, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, float scale,
+                       int32_t sliding_window, attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_prefill_status_string(int status);
 

@@ -256,3 +256,74 @@ def test_chunked_empty_queries_are_a_no_op_without_hip():
         a[key] = mutate(a[key], data=None)
     assert call_chunked(**a) == B.ATTN_OK
     assert B.last_error() == ""
+
+
+# ---- attn_prefill_paged: pools, block table and key counts
+
+
+def paged_args(nq=64, n_pages=8, page=64, hq=32, hkv=1, d=128):
+    a = base_args(n=nq, hq=hq, hkv=hkv, d=d)
+    a["k"] = mutate(a["k"], n_tokens=n_pages * page)
+    a["v"] = mutate(a["v"], n_tokens=n_pages * page)
+    a["paged"] = B.AttnPagedKV(FAKE + (5 << 30), FAKE + (6 << 30), 4, page)
+    return a
+
+
+def call_paged(**kw):
+    return B.call_raw_paged(kw["q"], kw["k"], kw["v"], kw["out"], kw["seqlens"],
+                            kw["paged"], kw["n_q_heads"], kw["n_kv_heads"],
+                            kw["head_dim"], kw["scale"], kw["sliding_window"], None)
+
+
+def _pg(a, **kw):
+    c = B.AttnPagedKV.from_buffer_copy(a["paged"])
+    for key, val in kw.items():
+        setattr(c, key, val)
+    return with_(a, paged=c)
+
+
+BAD_PAGED = [
+    ("page_size_not_multiple_of_64", lambda a: _pg(a, page_size=48),
+     B.ATTN_ERR_UNSUPPORTED, "page_size 48"),
+    ("page_size_zero", lambda a: _pg(a, page_size=0), B.ATTN_ERR_INVALID_ARG, "page_size 0"),
+    ("table_stride_zero", lambda a: _pg(a, table_stride=0), B.ATTN_ERR_INVALID_ARG,
+     "table_stride 0"),
+    ("null_block_table", lambda a: _pg(a, block_table=None), B.ATTN_ERR_INVALID_ARG,
+     "block_table"),
+    ("null_seqlens_k", lambda a: _pg(a, seqlens_k=None), B.ATTN_ERR_INVALID_ARG,
+     "seqlens_k"),
+    ("pool_not_whole_pages", lambda a: with_(a, k=mutate(a["k"], n_tokens=500),
+                                             v=mutate(a["v"], n_tokens=500)),
+     B.ATTN_ERR_INVALID_ARG, "not a multiple of page_size"),
+    ("pools_differ", lambda a: with_(a, v=mutate(a["v"], n_tokens=448)),
+     B.ATTN_ERR_INVALID_ARG, "k 512 v 448"),
+    ("empty_pool", lambda a: with_(a, k=mutate(a["k"], n_tokens=0, data=None),
+                                   v=mutate(a["v"], n_tokens=0, data=None)),
+     B.ATTN_ERR_INVALID_ARG, "k and v have none"),
+    ("table_capacity_beyond_int32", lambda a: _pg(a, table_stride=1 << 30),
+     B.ATTN_ERR_UNSUPPORTED, "exceeds int32"),
+]
+
+
+@pytest.mark.parametrize("name,mut,status,frag", BAD_PAGED, ids=[b[0] for b in BAD_PAGED])
+def test_paged_bad_argument_rejected_on_host(name, mut, status, frag):
+    rc = call_paged(**mut(paged_args()))
+    assert rc == status, (rc, B.last_error())
+    assert frag in B.last_error(), B.last_error()
+
+
+def test_paged_null_descriptor_rejected():
+    lib = B.load_library()
+    a = paged_args()
+    rc = lib.attn_prefill_paged(ctypes.byref(a["q"]), ctypes.byref(a["k"]),
+                                ctypes.byref(a["v"]), ctypes.byref(a["out"]),
+                                ctypes.byref(a["seqlens"]), None, 32, 1, 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "paged is NULL" in B.last_error()
+
+
+def test_paged_empty_queries_are_a_no_op_without_hip():
+    a = paged_args(nq=0)
+    for key in ("q", "out"):
+        a[key] = mutate(a[key], data=None)
+    assert call_paged(**a) == B.ATTN_OK
+    assert B.last_error() == ""

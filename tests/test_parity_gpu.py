@@ -400,3 +400,105 @@ def test_chunked_more_queries_than_keys_is_memory_safe():
                                     [0, 4], 4, 1, w.attn_scale, 0)
     assert np.all(want[:6] == 0.0)
     check("chunk_short_kv", to64(out), want)
+
+
+# ------------------------------------------------------------ paged K/V
+def to_paged(inp, page, seed, spare=3):
+    """Scatters a chunked input's packed K/V into page pools in a seeded
+    random page order; slots no sequence owns hold NaN, so that a wrong
+    page or slot read shows up in the output."""
+    rng = np.random.default_rng(seed)
+    kv_lengths = inp["kv_lengths"]
+    cu_k = inp["cu_seqlens_k"].tolist()
+    n_blocks = [(n + page - 1) // page for n in kv_lengths]
+    n_pages = sum(n_blocks) + spare
+    perm = rng.permutation(n_pages)
+    width = max(1, max(n_blocks))
+    table = np.full((len(kv_lengths), width), n_pages + 5, dtype=np.int32)
+    k, v = inp["k"], inp["v"]
+    k_pool = torch.full((n_pages * page,) + tuple(k.shape[1:]), float("nan"), dtype=k.dtype)
+    v_pool = torch.full((n_pages * page,) + tuple(v.shape[1:]), float("nan"), dtype=v.dtype)
+    used = 0
+    for s, n in enumerate(kv_lengths):
+        for b in range(n_blocks[s]):
+            pg = int(perm[used])
+            used += 1
+            table[s, b] = pg
+            lo, hi = cu_k[s] + b * page, min(cu_k[s] + n, cu_k[s] + (b + 1) * page)
+            k_pool[pg * page:pg * page + (hi - lo)] = k[lo:hi]
+            v_pool[pg * page:pg * page + (hi - lo)] = v[lo:hi]
+    return k_pool, v_pool, table
+
+
+def run_paged(inp, k_pool, v_pool, table, page, hq, hkv, scale, window):
+    dev = torch.device("cuda:0")
+    q = inp["q"].to(dev)
+    out = torch.empty(q.shape[0], hq, 128, dtype=torch.bfloat16, device=dev)
+    binding.attn_prefill_paged(
+        q, k_pool.to(dev), v_pool.to(dev), out, inp["cu_seqlens"].to(dev),
+        torch.from_numpy(table).to(dev),
+        torch.tensor(inp["kv_lengths"], dtype=torch.int32, device=dev), page, hq, hkv,
+        128, scale, window)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("page", [64, 128, 256])
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2)])
+def test_paged_grid_packed(page, hq, hkv):
+    lq = [a for a, _ in CHUNK_PAIRS]
+    hist = [b - a for a, b in CHUNK_PAIRS]
+    w = workloads.custom(f"paged_grid_p{page}_h{hq}x{hkv}", lq, hq, hkv, seed=81,
+                         history=hist)
+    inp = workloads.make_inputs(w)
+    k_pool, v_pool, table = to_paged(inp, page, seed=page + hq)
+    for win in (0, 63, 256):
+        _announce(f"{w.name} W={win}")
+        out = run_paged(inp, k_pool, v_pool, table, page, hq, hkv, w.attn_scale, win)
+        want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                      inp["kv_lengths"], page, hq, hkv, w.attn_scale, win)
+        check(f"paged_grid_p{page}_h{hq}x{hkv}_w{win}", to64(out), want)
+
+
+def test_paged_dtype_fp32q_fp16kv():
+    w = workloads.custom("paged_fp32q_fp16kv", [190, 33, 400], 8, 2, q_dtype="fp32",
+                         kv_dtype="fp16", seed=82, history=[500, 0, 129])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    k_pool, v_pool, table = to_paged(inp, 128, seed=5)
+    out = run_paged(inp, k_pool, v_pool, table, 128, 8, 2, w.attn_scale, 0)
+    want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                  inp["kv_lengths"], 128, 8, 2, w.attn_scale, 0)
+    check(w.name, to64(out), want)
+
+
+def test_paged_in_page_order_equals_chunked_bitwise():
+    """Pages laid out in position order give the packed chunked result bit
+    for bit (same tiles, same arithmetic)."""
+    w = workloads.custom("paged_identity", [256, 64], 8, 1, seed=83, history=[128, 0])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    page = 64
+    # one sequence's keys per run of pages, in order: a pool equal to the
+    # packed K/V, since both lengths are multiples of the page size
+    k_pool, v_pool = inp["k"], inp["v"]
+    table = np.array([[0, 1, 2, 3, 4, 5], [6, 0, 0, 0, 0, 0]], dtype=np.int32)
+    a = run_paged(inp, k_pool, v_pool, table, page, 8, 1, w.attn_scale, 0).clone()
+    b = run_gpu(inp, 8, 1, 128, w.attn_scale, 0)
+    assert torch.equal(a, b)
+
+
+def test_paged_full_size_sampled():
+    w = workloads.WORKLOADS["chunk2048_hist6144_32q1kv_outliers"]
+    _announce(f"paged full-size {w.name}")
+    inp = workloads.make_inputs(w)
+    k_pool, v_pool, table = to_paged(inp, 256, seed=7)
+    out = run_paged(inp, k_pool, v_pool, table, 256, w.n_q_heads, w.n_kv_heads,
+                    w.attn_scale, 0)
+    rows = workloads.sample_rows(inp["lengths"], w.n_q_heads, 256, seed=w.seed)
+    want = oracle.attention_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                 w.n_q_heads, w.n_kv_heads, w.attn_scale, 0, rows,
+                                 cu_seqlens_k=inp["cu_seqlens_k"])
+    got = to64(out)
+    check(f"paged_{w.name}_sampled{len(rows)}", np.stack([got[t, h] for t, h in rows]), want)
+    assert np.all(np.isfinite(got))
