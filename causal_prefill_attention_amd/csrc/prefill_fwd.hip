@@ -91,10 +91,12 @@ struct Cfg {
   static constexpr int OCTS = HDIM / 8;   // 16-byte chunks per row
   // Group A's 256 threads stage K, group B's stage V.
   static constexpr int STAGERS = kThreads / 2;
-  static constexpr int K_CHUNKS = kBN * OCTS / STAGERS;  // 16-byte K chunks per thread
-  static constexpr int V_UNITS = (kBN / 4) * OCTS / STAGERS;  // 4-key x 8-d V units
-  static_assert(K_CHUNKS * STAGERS == kBN * OCTS, "K tile split");
-  static_assert(V_UNITS * STAGERS == (kBN / 4) * OCTS, "V tile split");
+  static constexpr int K_TOTAL = kBN * OCTS;         // 16-byte K chunks per tile
+  static constexpr int V_TOTAL = (kBN / 4) * OCTS;   // 4-key x 8-d V units per tile
+  static constexpr int K_CHUNKS = (K_TOTAL + STAGERS - 1) / STAGERS;  // per thread
+  static constexpr int V_UNITS = (V_TOTAL + STAGERS - 1) / STAGERS;   // per thread
+  static constexpr int NPV = DBLK * (kBN / 16);  // P.V MFMAs per tile
+  static constexpr int NS = DCH * (kBN / 32);    // score MFMAs per tile
 };
 
 // ---------------------------------------------------------------- element io
@@ -324,8 +326,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
       const int chunk = stid + i * C::STAGERS;
-      kst[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          r, (chunk / C::OCTS) * k_row_bytes + 16 * (chunk % C::OCTS), 0, 0);
+      if (C::K_TOTAL % C::STAGERS == 0 || chunk < C::K_TOTAL)
+        kst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            r, (chunk / C::OCTS) * k_row_bytes + 16 * (chunk % C::OCTS), 0, 0);
     }
   };
   auto gload_v = [&](int kv0) {
@@ -337,10 +340,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
       const int unit = stid + u * C::STAGERS;
       const int kq = unit % (kBN / 4);
       const int oct = unit / (kBN / 4);
+      if (C::V_TOTAL % C::STAGERS == 0 || unit < C::V_TOTAL) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vst[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
-            r, (4 * kq + i) * v_row_bytes + 16 * oct, 0, 0);
+        for (int i = 0; i < 4; ++i)
+          vst[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
+              r, (4 * kq + i) * v_row_bytes + 16 * oct, 0, 0);
+      }
     }
   };
   // K row-major into stage `st`.
@@ -349,8 +354,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
       const int chunk = stid + i * C::STAGERS;
-      *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
-          kv_to_bf16(KVT(), kst[i]);
+      if (C::K_TOTAL % C::STAGERS == 0 || chunk < C::K_TOTAL)
+        *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
+            kv_to_bf16(KVT(), kst[i]);
     }
   };
   // V transposed into stage `st` with the key order of the S^T accumulator:
@@ -361,6 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 #pragma unroll
     for (int u = 0; u < C::V_UNITS; ++u) {
       const int unit = stid + u * C::STAGERS;
+      if (C::V_TOTAL % C::STAGERS != 0 && unit >= C::V_TOTAL) continue;
       const int kq = unit % (kBN / 4);
       const int oct = unit / (kBN / 4);
       const int qq = kq & 3;
@@ -426,39 +433,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     }
   };
   // Matrix slot of tile j when both P(j-1)V(j-1) and S(j) are needed, as one
-  // straight-line block: the 16 P.V MFMAs (four accumulator chains), then
-  // the 16 score MFMAs, with every LDS operand read kAhead MFMAs ahead
+  // straight-line block: the NPV P.V MFMAs (DBLK accumulator chains), then
+  // the NS score MFMAs, with every LDS operand read kAhead MFMAs ahead
   // (across the boundary between the two products, too).
   auto matrix_fused = [&](int kst_i, int vst_i) {
     const uint16_t* ks = kstage0 + kst_i * C::K_ELEMS;
     const uint16_t* vs = vstage0 + vst_i * C::V_ELEMS;
-    static_assert(C::DBLK * kKT == 16 && C::DCH * kKB == 16, "32-MFMA matrix slot");
-    // operand i < 16: V^T for P.V step i (kt-major over the 4 output blocks);
-    // i >= 16: K for score step i - 16 (d-chunk-major over the 2 key blocks)
+    constexpr int NPV = C::NPV, N = C::NPV + C::NS;
+    // operand i < NPV: V^T for P.V step i (kt-major over the output blocks);
+    // i >= NPV: K for score step i - NPV (d-chunk-major over the key blocks)
     auto operand = [&](int i) -> bf16x8_t {
-      if (i >= 16) {
-        const int c = (i - 16) >> 1, kb = i & 1;
+      if (i >= NPV) {
+        const int c = (i - NPV) / kKB, kb = (i - NPV) % kKB;
         return *reinterpret_cast<const bf16x8_t*>(ks + (32 * kb + col) * C::KSTR + 16 * c +
                                                   8 * half);
       }
-      const int kt = i >> 2, c = i & 3;
+      const int kt = i / C::DBLK, c = i % C::DBLK;
       return *reinterpret_cast<const bf16x8_t*>(vs + (32 * c + col) * C::VSTR + 16 * kt +
                                                 8 * half);
     };
-    constexpr int kAhead = 8;
+    constexpr int kAhead = N < 8 ? N : 8;
     bf16x8_t buf[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) buf[i] = operand(i);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < N; ++i) {
       const bf16x8_t a = buf[i % kAhead];
-      if (i + kAhead < 32) buf[i % kAhead] = operand(i + kAhead);
-      if (i >= 16) {
-        const int c = (i - 16) >> 1, kb = i & 1;
+      if (i + kAhead < N) buf[i % kAhead] = operand(i + kAhead);
+      if (i >= NPV) {
+        const int c = (i - NPV) / kKB, kb = (i - NPV) % kKB;
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? (f32x16_t){} : s[kb],
                                                         0, 0, 0);
       } else {
-        const int kt = i >> 2, c = i & 3;
+        const int kt = i / C::DBLK, c = i % C::DBLK;
         o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
       }
     }
@@ -466,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     // last kAhead MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 32 - kAhead; ++i) {
+    for (int i = 0; i < N - kAhead; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -651,6 +658,16 @@ hipError_t launch_one(PrefillParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int HDIM>
+hipError_t launch_dtypes(const PrefillParams& p, DType q_dtype, DType kv_dtype,
+                         hipStream_t stream) {
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_one<HDIM, BF16, BF16>(p, stream);
+  if (q_dtype == kBF16 && kv_dtype == kFP16) return launch_one<HDIM, BF16, FP16>(p, stream);
+  if (q_dtype == kFP32 && kv_dtype == kBF16) return launch_one<HDIM, FP32, BF16>(p, stream);
+  if (q_dtype == kFP32 && kv_dtype == kFP16) return launch_one<HDIM, FP32, FP16>(p, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int prefill_min_block_m(int /*head_dim*/) { return kBM; }
@@ -659,12 +676,8 @@ int prefill_kv_tile(int /*head_dim*/) { return kBN; }
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
                           DType kv_dtype, hipStream_t stream) {
-  if (head_dim == 128) {
-    if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_one<128, BF16, BF16>(p, stream);
-    if (q_dtype == kBF16 && kv_dtype == kFP16) return launch_one<128, BF16, FP16>(p, stream);
-    if (q_dtype == kFP32 && kv_dtype == kBF16) return launch_one<128, FP32, BF16>(p, stream);
-    if (q_dtype == kFP32 && kv_dtype == kFP16) return launch_one<128, FP32, FP16>(p, stream);
-  }
+  if (head_dim == 128) return launch_dtypes<128>(p, q_dtype, kv_dtype, stream);
+  if (head_dim == 64) return launch_dtypes<64>(p, q_dtype, kv_dtype, stream);
   return hipErrorInvalidValue;
 }
 

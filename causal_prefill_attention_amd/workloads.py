@@ -117,6 +117,10 @@ WORKLOADS: Dict[str, Workload] = {
     "chunk2048_hist6144_32q1kv_outliers": Workload(
         "chunk2048_hist6144_32q1kv_outliers", 5, (2048,), 32, 1, _D,
         k_outlier_frac=0.01, scale=_SCALE, history=(6144,)),
+    # the long prefill with 64-d heads
+    "d64_8192tok_32q1kv_outliers": Workload(
+        "d64_8192tok_32q1kv_outliers", 7, (8192,), 32, 1, 64,
+        k_outlier_frac=0.01, scale=1.0 / 8.0),
     # a packed batch of chunks with ragged histories, GQA 4:1
     "chunks8_gqa32q8kv_history": Workload(
         "chunks8_gqa32q8kv_history", 6, (300, 1, 64, 1000, 129, 0, 77, 512),

@@ -40,7 +40,7 @@ def test_status_strings_and_head_dims():
     for code in (B.ATTN_OK, B.ATTN_ERR_INVALID_ARG, B.ATTN_ERR_UNSUPPORTED,
                  B.ATTN_ERR_HIP, 99):
         assert lib.attn_prefill_status_string(code)
-    assert B.supported_head_dims() == [128]
+    assert B.supported_head_dims() == [64, 128]
     assert lib.attn_prefill_version() >= 100
 
 
@@ -87,8 +87,8 @@ BAD = [
      B.ATTN_ERR_INVALID_ARG, "multiple"),
     ("head_dim_256_unsupported", lambda a: with_(a, head_dim=256),
      B.ATTN_ERR_UNSUPPORTED, "head_dim 256"),
-    ("head_dim_64_unsupported", lambda a: with_(a, head_dim=64),
-     B.ATTN_ERR_UNSUPPORTED, "head_dim 64"),
+    ("head_dim_96_unsupported", lambda a: with_(a, head_dim=96),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 96"),
     ("head_dim_zero", lambda a: with_(a, head_dim=0), B.ATTN_ERR_INVALID_ARG, "head_dim"),
     ("scale_nan", lambda a: with_(a, scale=float("nan")), B.ATTN_ERR_INVALID_ARG, "scale"),
     ("scale_inf", lambda a: with_(a, scale=float("inf")), B.ATTN_ERR_INVALID_ARG, "scale"),
@@ -224,8 +224,8 @@ BAD_CHUNKED = [
     ("k_stride_beyond_buffer_range",
      lambda a: with_(a, k=mutate(a["k"], token_stride=1 << 24)),
      B.ATTN_ERR_UNSUPPORTED, "k: token stride"),
-    ("head_dim_64_unsupported", lambda a: with_(a, head_dim=64),
-     B.ATTN_ERR_UNSUPPORTED, "head_dim 64"),
+    ("head_dim_96_unsupported", lambda a: with_(a, head_dim=96),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 96"),
     ("out_aliases_v", lambda a: with_(a, out=mutate(a["out"], data=a["v"].data + 4096)),
      B.ATTN_ERR_INVALID_ARG, "overlaps"),
 ]

@@ -430,15 +430,15 @@ def to_paged(inp, page, seed, spare=3):
     return k_pool, v_pool, table
 
 
-def run_paged(inp, k_pool, v_pool, table, page, hq, hkv, scale, window):
+def run_paged(inp, k_pool, v_pool, table, page, hq, hkv, scale, window, d=128):
     dev = torch.device("cuda:0")
     q = inp["q"].to(dev)
-    out = torch.empty(q.shape[0], hq, 128, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(q.shape[0], hq, d, dtype=torch.bfloat16, device=dev)
     binding.attn_prefill_paged(
         q, k_pool.to(dev), v_pool.to(dev), out, inp["cu_seqlens"].to(dev),
         torch.from_numpy(table).to(dev),
         torch.tensor(inp["kv_lengths"], dtype=torch.int32, device=dev), page, hq, hkv,
-        128, scale, window)
+        d, scale, window)
     torch.cuda.synchronize()
     return out
 
@@ -502,3 +502,44 @@ def test_paged_full_size_sampled():
     got = to64(out)
     check(f"paged_{w.name}_sampled{len(rows)}", np.stack([got[t, h] for t, h in rows]), want)
     assert np.all(np.isfinite(got))
+
+
+# ------------------------------------------------------------ head_dim 64
+D64_LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 257, 0, 1, 200, 600]
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2), (6, 6)])
+def test_head_dim_64_packed(hq, hkv):
+    w = workloads.custom(f"d64_h{hq}x{hkv}", D64_LENGTHS, hq, hkv, head_dim=64, seed=91)
+    inp = workloads.make_inputs(w)
+    for win in (0, 1, 64, 129):
+        for scale in (1 / 8.0, -0.5):
+            _announce(f"{w.name} W={win} s={scale}")
+            out = run_gpu(inp, hq, hkv, 64, scale, win)
+            check(f"d64_h{hq}x{hkv}_w{win}_s{scale}", to64(out),
+                  oracle_of(inp, hq, hkv, scale, win))
+
+
+@pytest.mark.parametrize("qd,kvd", [("fp32", "fp16"), ("bf16", "fp16"), ("fp32", "bf16")])
+def test_head_dim_64_dtypes(qd, kvd):
+    w = workloads.custom(f"d64_{qd}_{kvd}", [300, 1, 77], 8, 2, head_dim=64, q_dtype=qd,
+                         kv_dtype=kvd, seed=92)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    out = run_gpu(inp, 8, 2, 64, w.attn_scale, 0)
+    check(w.name, to64(out), oracle_of(inp, 8, 2, w.attn_scale, 0))
+
+
+def test_head_dim_64_chunked_and_paged():
+    w = workloads.custom("d64_chunked", [190, 33, 400, 1], 8, 1, head_dim=64, seed=93,
+                         history=[500, 0, 129, 1000])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    for win in (0, 100):
+        out = run_gpu(inp, 8, 1, 64, w.attn_scale, win)
+        check(f"d64_chunked_w{win}", to64(out), oracle_of(inp, 8, 1, w.attn_scale, win))
+    k_pool, v_pool, table = to_paged(inp, 128, seed=11)
+    out = run_paged(inp, k_pool, v_pool, table, 128, 8, 1, w.attn_scale, 0, d=64)
+    want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                  inp["kv_lengths"], 128, 8, 1, w.attn_scale, 0)
+    check("d64_paged", to64(out), want)
