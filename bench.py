@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 KERNEL_SOURCES = [
     os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "prefill_fwd.hip"),
     os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "prefill_params.h"),
+    os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "device_common.h"),
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -171,7 +172,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        if cuk is None:
+        if w.decode:
+            binding.attn_decode(q, k, v, out, cuk, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                w.attn_scale, w.window, stream=stream)
+        elif cuk is None:
             binding.attn_prefill(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads,
                                  w.head_dim, w.attn_scale, w.window, stream=stream)
         else:
@@ -203,6 +207,15 @@ def main():
     achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = measure.PEAK_BF16_TFLOPS
     traffic = load_traffic(name)
+    alg_bytes = measure.algorithmic_bytes(lengths, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                          w.q_dtype, w.kv_dtype, kv_lengths)
+    if w.decode:  # one query per sequence: the step streams K/V from HBM
+        roof = {"bound": "hbm", "achieved": round(alg_bytes / (avg_ms * 1e-3) / 1e9, 1),
+                "peak": measure.PEAK_HBM_GBS, "unit": "GB/s"}
+        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
 
     line = {
         "metric": "causal prefill attention TFLOP/s and % of bf16 MFMA peak "
@@ -235,17 +248,11 @@ def main():
             "causal_flops": flops,
         },
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": round(peak, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            **roof,
             "traffic": traffic,
             "kernel_avg_us": round(avg_ms * 1e3, 2),
             "kernel_min_us": round(durs[0] * 1e3, 2),
-            "algorithmic_bytes": measure.algorithmic_bytes(
-                lengths, w.n_q_heads, w.n_kv_heads, w.head_dim, w.q_dtype, w.kv_dtype,
-                kv_lengths),
+            "algorithmic_bytes": alg_bytes,
         },
         "cpu_baseline": None,
     }

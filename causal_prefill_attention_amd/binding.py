@@ -24,7 +24,7 @@ ATTN_FP32 = 2
 
 #: Every symbol include/attn_prefill.h declares.
 EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_paged",
-           "attn_prefill_status_string",
+           "attn_decode", "attn_decode_paged", "attn_prefill_status_string",
            "attn_prefill_last_error", "attn_prefill_supported_head_dims",
            "attn_prefill_version")
 
@@ -84,6 +84,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
         ctypes.POINTER(AttnSeqlens), ctypes.POINTER(AttnPagedKV), ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode.argtypes = [
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnSeqlens), ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_decode_paged.restype = ctypes.c_int
+    lib.attn_decode_paged.argtypes = [
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnPagedKV), ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
     lib.attn_prefill_status_string.restype = ctypes.c_char_p
     lib.attn_prefill_status_string.argtypes = [ctypes.c_int]
     lib.attn_prefill_last_error.restype = ctypes.c_char_p
@@ -145,6 +157,30 @@ def call_raw_paged(q: AttnTensor, k_pool: AttnTensor, v_pool: AttnTensor,
         ctypes.byref(q), ctypes.byref(k_pool), ctypes.byref(v_pool), ctypes.byref(out),
         ctypes.byref(seqlens_q), ctypes.byref(paged), int(n_q_heads), int(n_kv_heads),
         int(head_dim), float(scale), int(sliding_window), ctypes.c_void_p(stream))
+
+
+def call_raw_decode(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
+                    seqlens_k: AttnSeqlens, n_q_heads: int, n_kv_heads: int,
+                    head_dim: int, scale: float, sliding_window: int,
+                    stream: Optional[int] = None) -> int:
+    """Calls ``attn_decode`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                           ctypes.byref(out), ctypes.byref(seqlens_k), int(n_q_heads),
+                           int(n_kv_heads), int(head_dim), float(scale),
+                           int(sliding_window), ctypes.c_void_p(stream))
+
+
+def call_raw_decode_paged(q: AttnTensor, k_pool: AttnTensor, v_pool: AttnTensor,
+                          out: AttnTensor, paged: AttnPagedKV, n_q_heads: int,
+                          n_kv_heads: int, head_dim: int, scale: float,
+                          sliding_window: int, stream: Optional[int] = None) -> int:
+    """Calls ``attn_decode_paged`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_decode_paged(ctypes.byref(q), ctypes.byref(k_pool), ctypes.byref(v_pool),
+                                 ctypes.byref(out), ctypes.byref(paged), int(n_q_heads),
+                                 int(n_kv_heads), int(head_dim), float(scale),
+                                 int(sliding_window), ctypes.c_void_p(stream))
 
 
 def _dtype_code(t) -> int:
@@ -230,6 +266,40 @@ def attn_prefill_paged(q, k_pool, v_pool, out, cu_seqlens_q, block_table, seqlen
     status = call_raw_paged(describe(q), describe(k_pool), describe(v_pool), describe(out),
                             sq, pg, n_q_heads, n_kv_heads, head_dim, scale,
                             sliding_window, _stream_handle(q, stream))
+    if status != ATTN_OK:
+        raise AttnPrefillError(status, last_error())
+
+
+def attn_decode(q, k, v, out, cu_seqlens_k, n_q_heads: int, n_kv_heads: int,
+                head_dim: int, scale: float, sliding_window: int = 0, stream=None) -> None:
+    """One decode step: q, out [n_seqs, heads, head_dim]; k, v packed by
+    ``cu_seqlens_k`` (each sequence's query sits after its last key)."""
+    sk = _seqlens(cu_seqlens_k, "cu_seqlens_k")
+    status = call_raw_decode(describe(q), describe(k), describe(v), describe(out), sk,
+                             n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
+                             _stream_handle(q, stream))
+    if status != ATTN_OK:
+        raise AttnPrefillError(status, last_error())
+
+
+def attn_decode_paged(q, k_pool, v_pool, out, block_table, seqlens_k, page_size: int,
+                      n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
+                      sliding_window: int = 0, stream=None) -> None:
+    """One decode step against a paged K/V cache (see attn_prefill_paged)."""
+    import torch
+
+    for t, name in ((block_table, "block_table"), (seqlens_k, "seqlens_k")):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if block_table.dim() != 2 or seqlens_k.dim() != 1:
+        raise ValueError("block_table must be [n_seqs, width], seqlens_k [n_seqs]")
+    if block_table.shape[0] != q.shape[0] or seqlens_k.shape[0] != q.shape[0]:
+        raise ValueError("block_table / seqlens_k rows must match the sequences")
+    pg = AttnPagedKV(block_table.data_ptr(), seqlens_k.data_ptr(), block_table.shape[1],
+                     page_size)
+    status = call_raw_decode_paged(describe(q), describe(k_pool), describe(v_pool),
+                                   describe(out), pg, n_q_heads, n_kv_heads, head_dim,
+                                   scale, sliding_window, _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
 

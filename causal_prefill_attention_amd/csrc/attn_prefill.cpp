@@ -143,6 +143,30 @@ int check_seqlens(const attn_seqlens* cu, const char* what) {
   return ATTN_OK;
 }
 
+// Checks shared by the paged entry points (prefill and decode).
+int check_paged(const attn_paged_kv* paged, int64_t Tk, int tile, int64_t n_queries,
+                int64_t* n_pages) {
+  if (paged->block_table == nullptr || paged->seqlens_k == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "paged: block_table and seqlens_k must be set");
+  if (paged->table_stride < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "paged: table_stride %d < 1", (int)paged->table_stride);
+  if (paged->page_size < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "paged: page_size %d < 1", (int)paged->page_size);
+  if (paged->page_size % tile != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "paged: page_size %d is not a multiple of %d",
+                (int)paged->page_size, tile);
+  if ((int64_t)paged->table_stride * paged->page_size > INT32_MAX)
+    return fail(ATTN_ERR_UNSUPPORTED, "paged: table_stride * page_size exceeds int32");
+  if (Tk % paged->page_size != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "paged: k has %lld token slots, not a multiple of "
+                "page_size %d", (long long)Tk, (int)paged->page_size);
+  *n_pages = Tk / paged->page_size;
+  if (n_queries > 0 && *n_pages == 0)
+    return fail(ATTN_ERR_INVALID_ARG, "q has %lld tokens but k and v have none",
+                (long long)n_queries);
+  return ATTN_OK;
+}
+
 // Debug-only host check of a paged cache's device metadata.
 int debug_validate_paged(const attn_seqlens* cu_q, int64_t n_q, const attn_paged_kv* pg,
                          int64_t n_pages, hipStream_t stream) {
@@ -228,27 +252,9 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
   }
   if ((rc = check_seqlens(cu_q, "cu_seqlens")) != ATTN_OK) return rc;
   int64_t n_pages = 0;
-  if (paged != nullptr) {
-    if (paged->block_table == nullptr || paged->seqlens_k == nullptr)
-      return fail(ATTN_ERR_INVALID_ARG, "paged: block_table and seqlens_k must be set");
-    if (paged->table_stride < 1)
-      return fail(ATTN_ERR_INVALID_ARG, "paged: table_stride %d < 1", (int)paged->table_stride);
-    if (paged->page_size < 1)
-      return fail(ATTN_ERR_INVALID_ARG, "paged: page_size %d < 1", (int)paged->page_size);
-    const int tile = attnp::prefill_kv_tile(head_dim);
-    if (paged->page_size % tile != 0)
-      return fail(ATTN_ERR_UNSUPPORTED, "paged: page_size %d is not a multiple of %d",
-                  (int)paged->page_size, tile);
-    if ((int64_t)paged->table_stride * paged->page_size > INT32_MAX)
-      return fail(ATTN_ERR_UNSUPPORTED, "paged: table_stride * page_size exceeds int32");
-    if (Tk % paged->page_size != 0)
-      return fail(ATTN_ERR_INVALID_ARG, "paged: k has %lld token slots, not a multiple of "
-                  "page_size %d", (long long)Tk, (int)paged->page_size);
-    n_pages = Tk / paged->page_size;
-    if (T > 0 && n_pages == 0)
-      return fail(ATTN_ERR_INVALID_ARG, "q has %lld tokens but k and v have none",
-                  (long long)T);
-  }
+  if (paged != nullptr &&
+      (rc = check_paged(paged, Tk, attnp::prefill_kv_tile(head_dim), T, &n_pages)) != ATTN_OK)
+    return rc;
   if (cu_k != nullptr) {
     if ((rc = check_seqlens(cu_k, "cu_seqlens_k")) != ATTN_OK) return rc;
     if (cu_k->n_seqs != cu_q->n_seqs)
@@ -331,9 +337,191 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
   return ATTN_OK;
 }
 
+// Debug-only host check of decode metadata: every sequence has >= 1 key.
+int debug_validate_decode(int64_t n_seqs, const attn_seqlens* cu_k, int64_t Tk,
+                          const attn_paged_kv* pg, int64_t n_pages, hipStream_t stream) {
+  std::vector<int32_t> lens((size_t)n_seqs);
+  int rc;
+  if (cu_k != nullptr) {
+    std::vector<int32_t> hk;
+    if ((rc = read_offsets(cu_k, hk, stream, "cu_seqlens_k")) != ATTN_OK) return rc;
+    if ((rc = check_offsets(hk, Tk, "cu_seqlens_k")) != ATTN_OK) return rc;
+    for (int64_t s = 0; s < n_seqs; ++s) lens[s] = hk[s + 1] - hk[s];
+  } else {
+    std::vector<int32_t> table((size_t)n_seqs * pg->table_stride);
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess)
+      e = hipMemcpy(lens.data(), pg->seqlens_k, lens.size() * sizeof(int32_t),
+                    hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+      e = hipMemcpy(table.data(), pg->block_table, table.size() * sizeof(int32_t),
+                    hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_HIP, "ATTN_PREFILL_VALIDATE: reading the paged metadata failed: %s",
+                  hipGetErrorString(e));
+    const int64_t cap = (int64_t)pg->table_stride * pg->page_size;
+    for (int64_t s = 0; s < n_seqs; ++s) {
+      if (lens[s] > cap)
+        return fail(ATTN_ERR_INVALID_ARG, "seqlens_k[%lld] = %d exceeds %lld", (long long)s,
+                    lens[s], (long long)cap);
+      const int used = (lens[s] + pg->page_size - 1) / pg->page_size;
+      for (int b = 0; b < used; ++b) {
+        const int32_t page = table[s * (size_t)pg->table_stride + b];
+        if (page < 0 || page >= n_pages)
+          return fail(ATTN_ERR_INVALID_ARG, "block_table[%lld][%d] = %d outside [0, %lld)",
+                      (long long)s, b, page, (long long)n_pages);
+      }
+    }
+  }
+  for (int64_t s = 0; s < n_seqs; ++s)
+    if (lens[s] < 1)
+      return fail(ATTN_ERR_INVALID_ARG, "sequence %lld has %d keys (decode needs >= 1)",
+                  (long long)s, lens[s]);
+  return ATTN_OK;
+}
+
+// Both decode entry points: exactly one of cu_k and paged is set.
+int run_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+               const attn_tensor* out, const attn_seqlens* cu_k, const attn_paged_kv* paged,
+               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+               int32_t sliding_window, attn_stream_t stream) {
+  g_last_error.clear();
+  if (n_q_heads < 1 || n_kv_heads < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
+                (int)n_q_heads, (int)n_kv_heads);
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                (int)n_q_heads, (int)n_kv_heads);
+  if (head_dim < 1) return fail(ATTN_ERR_INVALID_ARG, "head_dim %d < 1", (int)head_dim);
+  if (head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "no decode kernel for head_dim %d (supported: 128)",
+                (int)head_dim);
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
+  if (sliding_window < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "sliding_window %d < 0 (0 = off)", (int)sliding_window);
+  int rc;
+  if ((rc = check_tensor(q, "q", n_q_heads, head_dim)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(k, "k", n_kv_heads, head_dim)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(v, "v", n_kv_heads, head_dim)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(out, "out", n_q_heads, head_dim)) != ATTN_OK) return rc;
+  if (q->dtype != ATTN_BF16 && q->dtype != ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "q dtype must be BF16 or FP32");
+  if (k->dtype != v->dtype) return fail(ATTN_ERR_UNSUPPORTED, "k and v dtypes differ");
+  if (k->dtype != ATTN_BF16 && k->dtype != ATTN_FP16)
+    return fail(ATTN_ERR_UNSUPPORTED, "k/v dtype must be BF16 or FP16");
+  if (out->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "out dtype must be BF16");
+  const int64_t n_seqs = q->n_tokens;  // one query token per sequence
+  const int64_t Tk = k->n_tokens;
+  if (out->n_tokens != n_seqs)
+    return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: q %lld out %lld", (long long)n_seqs,
+                (long long)out->n_tokens);
+  if (v->n_tokens != Tk)
+    return fail(ATTN_ERR_INVALID_ARG, "n_tokens differ: k %lld v %lld", (long long)Tk,
+                (long long)v->n_tokens);
+  if (n_seqs == 0) return ATTN_OK;  // no sequence, nothing to compute or write
+  int64_t n_pages = 0;
+  if (cu_k != nullptr) {
+    if ((rc = check_seqlens(cu_k, "cu_seqlens_k")) != ATTN_OK) return rc;
+    if (cu_k->n_seqs != n_seqs)
+      return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k has %d sequences, q has %lld tokens",
+                  (int)cu_k->n_seqs, (long long)n_seqs);
+    if (n_seqs > 0 && Tk == 0)
+      return fail(ATTN_ERR_INVALID_ARG, "q has %lld tokens but k and v have none",
+                  (long long)n_seqs);
+  } else if ((rc = check_paged(paged, Tk, attnp::decode_kv_tile(), n_seqs, &n_pages)) !=
+             ATTN_OK) {
+    return rc;
+  }
+  for (const attn_tensor* t : {k, v}) {
+    if (Tk > 1 && t->token_stride * elem_bytes(t->dtype) * 64 > (int64_t)INT32_MAX)
+      return fail(ATTN_ERR_UNSUPPORTED,
+                  "%s: token stride of %lld bytes is too large (at most 32 MiB - 1 B)",
+                  t == k ? "k" : "v", (long long)(t->token_stride * elem_bytes(t->dtype)));
+  }
+  const Extent eo = extent_of(out, n_q_heads, head_dim);
+  if (overlaps(eo, extent_of(q, n_q_heads, head_dim)) ||
+      overlaps(eo, extent_of(k, n_kv_heads, head_dim)) ||
+      overlaps(eo, extent_of(v, n_kv_heads, head_dim)))
+    return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
+  const int64_t group = n_q_heads / n_kv_heads;
+  const int64_t blocks = n_seqs * n_kv_heads * ((group + 31) / 32);
+  if (blocks * 256 >= ((int64_t)1 << 32))
+    return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)blocks);
+  const char* dbg = getenv("ATTN_PREFILL_VALIDATE");
+  if (dbg != nullptr && dbg[0] == '1') {
+    if ((rc = debug_validate_decode(n_seqs, cu_k, Tk, paged, n_pages,
+                                    reinterpret_cast<hipStream_t>(stream))) != ATTN_OK)
+      return rc;
+  }
+
+  attnp::DecodeParams p;
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.out = out->data;
+  p.cu_seqlens_k = cu_k != nullptr ? cu_k->data : nullptr;
+  p.block_table = paged != nullptr ? paged->block_table : nullptr;
+  p.seqlens_k = paged != nullptr ? paged->seqlens_k : nullptr;
+  p.q_ts = q->token_stride;
+  p.q_hs = q->head_stride;
+  p.k_ts = k->token_stride;
+  p.k_hs = k->head_stride;
+  p.v_ts = v->token_stride;
+  p.v_hs = v->head_stride;
+  p.o_ts = out->token_stride;
+  p.o_hs = out->head_stride;
+  p.n_seqs = (int32_t)n_seqs;
+  p.n_q_heads = n_q_heads;
+  p.n_kv_heads = n_kv_heads;
+  p.group = (int32_t)group;
+  p.window = sliding_window;
+  p.n_tokens_k = (int32_t)Tk;
+  p.table_stride = paged != nullptr ? paged->table_stride : 0;
+  p.page_size = paged != nullptr ? paged->page_size : 0;
+  p.n_pages = (int32_t)n_pages;
+  const float log2e = 1.4426950408889634f;
+  if (scale == 0.f) {
+    p.score_mult = 1.f;
+    p.q_mult = 0.f;
+  } else {
+    p.score_mult = fabsf(scale) * log2e;
+    p.q_mult = scale < 0.f ? -1.f : 1.f;
+  }
+  const hipError_t e = attnp::launch_decode(p, head_dim, (attnp::DType)q->dtype,
+                                            (attnp::DType)k->dtype,
+                                            reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                const attn_tensor* out, const attn_seqlens* cu_seqlens_k, int32_t n_q_heads,
+                int32_t n_kv_heads, int32_t head_dim, float scale, int32_t sliding_window,
+                attn_stream_t stream) {
+  if (cu_seqlens_k == nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
+  }
+  return run_decode(q, k, v, out, cu_seqlens_k, nullptr, n_q_heads, n_kv_heads, head_dim, scale,
+                    sliding_window, stream);
+}
+
+int attn_decode_paged(const attn_tensor* q, const attn_tensor* k_pool, const attn_tensor* v_pool,
+                      const attn_tensor* out, const attn_paged_kv* paged, int32_t n_q_heads,
+                      int32_t n_kv_heads, int32_t head_dim, float scale, int32_t sliding_window,
+                      attn_stream_t stream) {
+  if (paged == nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "paged is NULL");
+  }
+  return run_decode(q, k_pool, v_pool, out, nullptr, paged, n_q_heads, n_kv_heads, head_dim,
+                    scale, sliding_window, stream);
+}
 
 int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                  const attn_tensor* out, const attn_seqlens* cu_seqlens,

@@ -53,19 +53,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "prefill_params.h"
 
 namespace attnp {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+using namespace dev;
 
 constexpr int kWave = 64;
 constexpr int kWaves = 8;      // two groups of four, one wave of each per SIMD
@@ -76,8 +70,6 @@ constexpr int kKT = kBN / 16;  // 16-key MFMA k-steps of the P.V contraction
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 // Lazy-max threshold (log2 units): p = 2^(t - m) may reach 2^kLazy before m moves.
 constexpr float kLazy = 8.0f;
-// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
-constexpr int kRsrcWord3 = 0x00020000;
 
 template <int HDIM>
 struct Cfg {
@@ -100,61 +92,6 @@ struct Cfg {
 };
 
 // ---------------------------------------------------------------- element io
-struct BF16 { typedef uint16_t T; };
-struct FP16 { typedef _Float16 T; };
-struct FP32 { typedef float T; };
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2_t r = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ u32x4_t load16(const void* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
-
-// Eight consecutive elements as float.
-__device__ __forceinline__ void load8f(const uint16_t* p, float* f) {
-  const u32x4_t u = load16(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(u[i] << 16);
-    f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ void load8f(const float* p, float* f) {
-  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[i] = a[i];
-    f[4 + i] = b[i];
-  }
-}
-
-// Raw 16-byte K/V chunk -> eight bf16 (identity for bf16 storage).
-__device__ __forceinline__ u32x4_t kv_to_bf16(BF16, u32x4_t raw) { return raw; }
-__device__ __forceinline__ u32x4_t kv_to_bf16(FP16, u32x4_t raw) {
-  const f16x8_t h = __builtin_bit_cast(f16x8_t, raw);
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2((float)h[2 * i], (float)h[2 * i + 1]);
-  return r;
-}
-
-// Value of the other half-wave's lane (l <-> l ^ 32) combined with ours.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------- work decode
 struct Work {

@@ -48,6 +48,40 @@ int prefill_min_block_m(int head_dim);
 // Keys per K/V tile; a paged cache's page_size must be a multiple of it.
 int prefill_kv_tile(int head_dim);
 
+// One decode step: one query token per sequence (the sequence's next
+// position) against its keys.  Passed to the decode kernel by value.
+struct DecodeParams {
+  const void* q;               // [n_seqs, n_q_heads, d]
+  const void* k;               // packed [Tk, n_kv_heads, d] or a paged pool
+  const void* v;
+  void* out;                   // [n_seqs, n_q_heads, d] bf16
+  const int32_t* cu_seqlens_k; // packed: n_seqs + 1 key offsets (device)
+  const int32_t* block_table;  // paged: [n_seqs * table_stride] (device)
+  const int32_t* seqlens_k;    // paged: [n_seqs] key counts (device)
+  int64_t q_ts, q_hs;
+  int64_t k_ts, k_hs;
+  int64_t v_ts, v_hs;
+  int64_t o_ts, o_hs;
+  int32_t n_seqs;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t group;               // n_q_heads / n_kv_heads
+  int32_t window;              // 0 = off
+  int32_t n_tokens_k;          // Tk of packed K/V (offsets clamp into [0, Tk])
+  int32_t table_stride;
+  int32_t page_size;           // 0 = packed
+  int32_t n_pages;
+  float score_mult;
+  float q_mult;
+};
+
+// Launches the decode kernel (head_dim 128, q bf16/fp32, kv bf16/fp16).
+hipError_t launch_decode(const DecodeParams& p, int head_dim, DType q_dtype, DType kv_dtype,
+                         hipStream_t stream);
+
+// Keys per decode tile; a paged cache's page_size must be a multiple of it.
+int decode_kv_tile();
+
 // Launches the kernel for (head_dim, q dtype, kv dtype) on `stream`; picks
 // the workgroup size and sets p.tile_slots.  Returns hipErrorInvalidValue if
 // no instantiation exists.

@@ -61,6 +61,7 @@ class Workload:
     k_outlier_mult: float = 30.0
     scale: Optional[float] = None  # None -> 1/sqrt(head_dim)
     history: Optional[Tuple[int, ...]] = None  # KV history per sequence (chunked)
+    decode: bool = False  # one query per sequence, run through the decode kernel
 
     @property
     def attn_scale(self) -> float:
@@ -81,6 +82,7 @@ class Workload:
             "k_outlier_frac": self.k_outlier_frac,
             "scale": self.attn_scale,
             **({"history": list(self.history)} if self.history else {}),
+            **({"decode": True} if self.decode else {}),
         }
 
 
@@ -121,6 +123,14 @@ WORKLOADS: Dict[str, Workload] = {
     "d64_8192tok_32q1kv_outliers": Workload(
         "d64_8192tok_32q1kv_outliers", 7, (8192,), 32, 1, 64,
         k_outlier_frac=0.01, scale=1.0 / 8.0),
+    # decode: 64 sequences of mixed length (512 .. 8191 keys), GQA 4:1
+    "decode64_gqa32q8kv_mixed": Workload(
+        "decode64_gqa32q8kv_mixed", 8, (1,) * 64, 32, 8, _D, scale=_SCALE,
+        history=tuple(511 + (s * 977) % 7680 for s in range(64)), decode=True),
+    # decode: 32 sequences of 8192 keys, MQA with 32 query heads
+    "decode32_mqa32q1kv_8192": Workload(
+        "decode32_mqa32q1kv_8192", 9, (1,) * 32, 32, 1, _D, scale=_SCALE,
+        history=(8191,) * 32, decode=True),
     # a packed batch of chunks with ragged histories, GQA 4:1
     "chunks8_gqa32q8kv_history": Workload(
         "chunks8_gqa32q8kv_history", 6, (300, 1, 64, 1000, 129, 0, 77, 512),

@@ -175,6 +175,33 @@ int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
                        int32_t n_kv_heads, int32_t head_dim, float scale,
                        int32_t sliding_window, attn_stream_t stream);
 
+/* Decode: one new query token per sequence (the batched last-token step).
+ * Sequence s's query q[s] sits at position Lk - 1 of its Lk keys and sees
+ * all of them (with a window W > 0 the last W).  This is
+ * attn_prefill_chunked with one query per sequence, computed by a kernel
+ * that puts the query heads sharing a KV head on the MFMA columns and
+ * splits each sequence's keys across four waves.
+ *   q, out: n_tokens = n_seqs ([n_seqs, heads, head_dim], any strides)
+ *   k, v:   packed keys, n_tokens = Tk, sequence s owning
+ *           [cu_seqlens_k[s], cu_seqlens_k[s+1]); cu_seqlens_k->n_seqs must
+ *           equal q->n_tokens
+ *   head_dim: 128 only (else ATTN_ERR_UNSUPPORTED)
+ * A sequence with no key (outside the contract) gets a zero row.  Other
+ * arguments, precision, ownership and errors as for attn_prefill. */
+int attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                const attn_tensor* out, const attn_seqlens* cu_seqlens_k,
+                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                float scale, int32_t sliding_window, attn_stream_t stream);
+
+/* Decode against a paged cache: as attn_decode with sequence s's
+ * Lk = seqlens_k[s] keys read through the block table (attn_paged_kv
+ * above; the table has q->n_tokens rows, page_size a multiple of 64). */
+int attn_decode_paged(const attn_tensor* q, const attn_tensor* k_pool,
+                      const attn_tensor* v_pool, const attn_tensor* out,
+                      const attn_paged_kv* paged, int32_t n_q_heads,
+                      int32_t n_kv_heads, int32_t head_dim, float scale,
+                      int32_t sliding_window, attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_prefill_status_string(int status);
 

@@ -5,6 +5,7 @@ leg of ``bench.py``; never by the library or its binding.
 """
 from .attention import (  # noqa: F401
     attention_chunked,
+    attention_decode,
     attention_head,
     attention_paged,
     attention_rows,

@@ -46,6 +46,10 @@ position ``j`` of sequence ``s`` is slot ``j % page_size`` of page
 ``block_table[s][j // page_size]``; ``seqlens_k[s]`` gives ``Lk``.  The result
 is ``attention_chunked`` on the keys and values gathered in position order.
 
+Decode (``attention_decode``): one new query per sequence, the batched
+last-token step of the m40-llm AGENTS.md page ("Current Progress"); it is
+``attention_chunked`` with ``Lq = 1`` for every sequence.
+
 The online-softmax recurrence that the GPU kernel uses (the fused MLA prefill
 commit on the atlas PR #69 page) is a reordering of steps 4-5 and is not
 used here.  The head grouping ``g = h // group`` is the consecutive GQA
@@ -68,6 +72,7 @@ __all__ = [
     "attention_varlen",
     "attention_chunked",
     "attention_paged",
+    "attention_decode",
     "gather_pages",
     "attention_rows",
     "visible_pairs",
@@ -263,6 +268,16 @@ def attention_paged(q, k_pool, v_pool, cu_seqlens_q, block_table, seqlens_k,
     v, _ = gather_pages(v_pool, block_table, seqlens_k, page_size)
     return attention_chunked(q, k, v, cu_seqlens_q, cu_k, n_q_heads, n_kv_heads,
                              scale, window, workers=workers)
+
+
+def attention_decode(q, k, v, cu_seqlens_k, n_q_heads: int, n_kv_heads: int,
+                     scale: float, window: int,
+                     workers: Optional[int] = None) -> np.ndarray:
+    """One query per sequence (``q``: ``[n_seqs, n_q_heads, d]``) against
+    the packed keys of ``cu_seqlens_k``."""
+    n = np.shape(q)[0]
+    return attention_chunked(q, k, v, list(range(n + 1)), cu_seqlens_k, n_q_heads,
+                             n_kv_heads, scale, window, workers=workers)
 
 
 def attention_rows(q, k, v, cu_seqlens, n_q_heads: int, n_kv_heads: int,

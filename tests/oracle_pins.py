@@ -367,6 +367,20 @@ def pin_paged_page_permutation_invariance(mod):
     assert np.max(np.abs(a - b)) <= 1e-12
 
 
+def pin_decode_is_the_last_prefill_row(mod):
+    # decoding the token after a prefix gives the single-pass prefill row of
+    # that token (query at the last position sees every earlier key)
+    rng = np.random.default_rng(51)
+    lengths, hq, hkv, d = [1, 6, 23, 40], 8, 2, 8
+    q, k, v = _rand(rng, lengths, hq, hkv, d)
+    cu = _cu(lengths)
+    for w in (0, 1, 5):
+        full = mod.attention_varlen(q, k, v, cu, hq, hkv, 0.6, w, workers=1)
+        last = [cu[s + 1] - 1 for s in range(len(lengths))]
+        got = mod.attention_decode(q[last], k, v, cu, hq, hkv, 0.6, w, workers=1)
+        assert np.max(np.abs(got - full[last])) <= 1e-12, w
+
+
 ALL_PINS = [
     pin_golden,
     pin_bruteforce,
@@ -385,4 +399,5 @@ ALL_PINS = [
     pin_chunks_reproduce_single_pass,
     pin_paged_bruteforce,
     pin_paged_page_permutation_invariance,
+    pin_decode_is_the_last_prefill_row,
 ]

@@ -327,3 +327,77 @@ def test_paged_empty_queries_are_a_no_op_without_hip():
         a[key] = mutate(a[key], data=None)
     assert call_paged(**a) == B.ATTN_OK
     assert B.last_error() == ""
+
+
+# ---- attn_decode / attn_decode_paged
+
+
+def decode_args(n_seqs=16, nk=4096, hq=32, hkv=8, d=128):
+    a = base_args(n=n_seqs, hq=hq, hkv=hkv, d=d)
+    a["k"] = mutate(a["k"], n_tokens=nk)
+    a["v"] = mutate(a["v"], n_tokens=nk)
+    a["seqlens_k"] = B.AttnSeqlens(FAKE + (5 << 30), n_seqs, 0)
+    return a
+
+
+def call_decode(**kw):
+    return B.call_raw_decode(kw["q"], kw["k"], kw["v"], kw["out"], kw["seqlens_k"],
+                             kw["n_q_heads"], kw["n_kv_heads"], kw["head_dim"],
+                             kw["scale"], kw["sliding_window"], None)
+
+
+BAD_DECODE = [
+    ("seq_count_differs_from_q", lambda a: with_(a, seqlens_k=B.AttnSeqlens(FAKE, 15, 0)),
+     B.ATTN_ERR_INVALID_ARG, "15 sequences"),
+    ("out_rows_differ", lambda a: with_(a, out=mutate(a["out"], n_tokens=15)),
+     B.ATTN_ERR_INVALID_ARG, "q 16 out 15"),
+    ("v_tokens_differ", lambda a: with_(a, v=mutate(a["v"], n_tokens=4095)),
+     B.ATTN_ERR_INVALID_ARG, "k 4096 v 4095"),
+    ("no_keys", lambda a: with_(a, k=mutate(a["k"], n_tokens=0, data=None),
+                                v=mutate(a["v"], n_tokens=0, data=None)),
+     B.ATTN_ERR_INVALID_ARG, "k and v have none"),
+    ("head_dim_64_has_no_decode_kernel", lambda a: with_(a, head_dim=64),
+     B.ATTN_ERR_UNSUPPORTED, "no decode kernel for head_dim 64"),
+    ("heads_not_multiple", lambda a: with_(a, n_q_heads=30),
+     B.ATTN_ERR_INVALID_ARG, "multiple"),
+    ("q_fp16_unsupported", lambda a: with_(a, q=mutate(a["q"], dtype=B.ATTN_FP16)),
+     B.ATTN_ERR_UNSUPPORTED, "q dtype"),
+    ("scale_nan", lambda a: with_(a, scale=float("nan")), B.ATTN_ERR_INVALID_ARG, "scale"),
+    ("out_aliases_k", lambda a: with_(a, out=mutate(a["out"], data=a["k"].data)),
+     B.ATTN_ERR_INVALID_ARG, "overlaps"),
+]
+
+
+@pytest.mark.parametrize("name,mut,status,frag", BAD_DECODE, ids=[b[0] for b in BAD_DECODE])
+def test_decode_bad_argument_rejected_on_host(name, mut, status, frag):
+    rc = call_decode(**mut(decode_args()))
+    assert rc == status, (rc, B.last_error())
+    assert frag in B.last_error(), B.last_error()
+
+
+def test_decode_null_arguments_rejected():
+    lib = B.load_library()
+    a = decode_args()
+    rc = lib.attn_decode(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                         ctypes.byref(a["out"]), None, 32, 8, 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "cu_seqlens_k is NULL" in B.last_error()
+    rc = lib.attn_decode_paged(ctypes.byref(a["q"]), ctypes.byref(a["k"]),
+                               ctypes.byref(a["v"]), ctypes.byref(a["out"]), None,
+                               32, 8, 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "paged is NULL" in B.last_error()
+
+
+def test_decode_paged_page_size_checked():
+    a = decode_args()
+    pg = B.AttnPagedKV(FAKE + (6 << 30), FAKE + (7 << 30), 8, 32)
+    rc = B.call_raw_decode_paged(a["q"], a["k"], a["v"], a["out"], pg, 32, 8, 128, 0.1, 0,
+                                 None)
+    assert rc == B.ATTN_ERR_UNSUPPORTED and "page_size 32" in B.last_error()
+
+
+def test_decode_empty_batch_is_a_no_op_without_hip():
+    a = decode_args(n_seqs=0)
+    for key in ("q", "out"):
+        a[key] = mutate(a[key], data=None)
+    assert call_decode(**a) == B.ATTN_OK
+    assert B.last_error() == ""

@@ -67,7 +67,10 @@ def run_gpu(inp, hq, hkv, d, scale, window, out=None):
     cu = inp["cu_seqlens"].to(dev)
     if out is None:
         out = torch.empty(q.shape[0], hq, d, dtype=torch.bfloat16, device=dev)
-    if "cu_seqlens_k" in inp:
+    if inp.get("decode"):
+        binding.attn_decode(q, k, v, out, inp["cu_seqlens_k"].to(dev), hq, hkv, d, scale,
+                            window)
+    elif "cu_seqlens_k" in inp:
         binding.attn_prefill_chunked(q, k, v, out, cu, inp["cu_seqlens_k"].to(dev),
                                      hq, hkv, d, scale, window)
     else:
@@ -299,6 +302,7 @@ def test_full_size_sampled(name):
     w = workloads.WORKLOADS[name]
     _announce(f"full-size {name}")
     inp = workloads.make_inputs(w)
+    inp["decode"] = w.decode
     out = run_gpu(inp, w.n_q_heads, w.n_kv_heads, w.head_dim, w.attn_scale, w.window)
     rows = workloads.sample_rows(inp["lengths"], w.n_q_heads, 256, seed=w.seed)
     want = oracle.attention_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
@@ -543,3 +547,102 @@ def test_head_dim_64_chunked_and_paged():
     want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
                                   inp["kv_lengths"], 128, 8, 1, w.attn_scale, 0)
     check("d64_paged", to64(out), want)
+
+
+# ---------------------------------------------------------------- decode
+DECODE_LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 4097]
+
+
+def decode_inputs(name, lengths, hq, hkv, seed, qd="bf16", kvd="bf16"):
+    w = workloads.custom(name, [1] * len(lengths), hq, hkv, seed=seed, q_dtype=qd,
+                         kv_dtype=kvd, history=[n - 1 for n in lengths])
+    inp = workloads.make_inputs(w)
+    inp["decode"] = True
+    return w, inp
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (8, 2), (4, 4), (64, 1), (40, 8)])
+def test_decode_grid(hq, hkv):
+    w, inp = decode_inputs(f"decode_grid_h{hq}x{hkv}", DECODE_LENGTHS, hq, hkv, seed=101)
+    for win in (0, 1, 64, 300):
+        for scale in (1 / math.sqrt(128), -0.7):
+            _announce(f"{w.name} W={win} s={scale:.3f}")
+            out = run_gpu(inp, hq, hkv, 128, scale, win)
+            want = oracle.attention_decode(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_k"],
+                                           hq, hkv, scale, win)
+            check(f"decode_grid_h{hq}x{hkv}_w{win}_s{scale:.3f}", to64(out), want)
+
+
+@pytest.mark.parametrize("qd,kvd", [("fp32", "fp16"), ("bf16", "fp16"), ("fp32", "bf16")])
+def test_decode_dtypes(qd, kvd):
+    w, inp = decode_inputs(f"decode_{qd}_{kvd}", [5, 700, 2048, 33], 16, 2, seed=102,
+                           qd=qd, kvd=kvd)
+    _announce(w.name)
+    out = run_gpu(inp, 16, 2, 128, w.attn_scale, 0)
+    want = oracle.attention_decode(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_k"], 16, 2,
+                                   w.attn_scale, 0)
+    check(w.name, to64(out), want)
+
+
+def test_decode_matches_prefill_last_rows():
+    """The decode step for the token after a prefix equals the prefill row
+    of that token (both on the GPU)."""
+    dev = torch.device("cuda:0")
+    lengths = [300, 1, 1000, 65]
+    w = workloads.custom("decode_vs_prefill", lengths, 32, 4, seed=103)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    full = to64(run_gpu(inp, 32, 4, 128, w.attn_scale, 0))
+    cu = inp["cu_seqlens"].tolist()
+    last = [cu[s + 1] - 1 for s in range(len(lengths))]
+    q = inp["q"][last].contiguous().to(dev)
+    out = torch.empty(len(lengths), 32, 128, dtype=torch.bfloat16, device=dev)
+    binding.attn_decode(q, inp["k"].to(dev), inp["v"].to(dev), out, inp["cu_seqlens"].to(dev),
+                        32, 4, 128, w.attn_scale, 0)
+    torch.cuda.synchronize()
+    diff = float(np.max(np.abs(to64(out) - full[last])))
+    sys.stdout.write(f"[decode] max |decode - prefill last row| = {diff}\n")
+    assert diff <= 2e-2
+
+
+def test_decode_paged_nan_pools():
+    w, inp = decode_inputs("decode_paged", DECODE_LENGTHS, 32, 2, seed=104)
+    _announce(w.name)
+    dev = torch.device("cuda:0")
+    for page in (64, 256):
+        k_pool, v_pool, table = to_paged(inp, page, seed=page)
+        out = torch.empty(len(DECODE_LENGTHS), 32, 128, dtype=torch.bfloat16, device=dev)
+        binding.attn_decode_paged(
+            inp["q"].to(dev), k_pool.to(dev), v_pool.to(dev), out,
+            torch.from_numpy(table).to(dev),
+            torch.tensor(inp["kv_lengths"], dtype=torch.int32, device=dev), page, 32, 2, 128,
+            w.attn_scale, 0)
+        torch.cuda.synchronize()
+        want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                      inp["kv_lengths"], page, 32, 2, w.attn_scale, 0)
+        check(f"decode_paged_p{page}", to64(out), want)
+
+
+def test_decode_strided_views_and_empty_sequence():
+    """q and out as strided views (head-major q); a sequence without keys
+    (outside the contract) gives a zero row; nothing outside out is written."""
+    dev = torch.device("cuda:0")
+    lengths = [40, 0, 300]
+    w = workloads.custom("decode_strided", [1, 1, 1], 8, 1, seed=105,
+                         history=[39, 0, 299])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    # the middle sequence has one key in the draw; give it none
+    cu_k = torch.tensor([0, 40, 40, 340], dtype=torch.int32)
+    k = torch.cat([inp["k"][:40], inp["k"][41:]])
+    v = torch.cat([inp["v"][:40], inp["v"][41:]])
+    qh = inp["q"].permute(1, 0, 2).contiguous().permute(1, 0, 2)  # head-major storage
+    ob = torch.full((5, 8, 128), 7.0, dtype=torch.bfloat16, device=dev)
+    out = ob[1:4]
+    binding.attn_decode(qh.to(dev), k.to(dev), v.to(dev), out, cu_k.to(dev), 8, 1, 128,
+                        w.attn_scale, 0)
+    torch.cuda.synchronize()
+    assert torch.all(ob[0].float() == 7.0) and torch.all(ob[4].float() == 7.0)
+    want = oracle.attention_decode(inp["q"], k, v, cu_k, 8, 1, w.attn_scale, 0)
+    assert np.all(want[1] == 0.0)
+    check("decode_strided", to64(out), want)
