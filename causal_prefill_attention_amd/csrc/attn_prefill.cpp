@@ -33,7 +33,7 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-const int32_t kHeadDims[] = {64, 128};
+const int32_t kHeadDims[] = {64, 128, 256};
 
 bool head_dim_supported(int32_t d) {
   for (int32_t x : kHeadDims)
@@ -219,7 +219,7 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
                 (int)n_q_heads, (int)n_kv_heads);
   if (head_dim < 1) return fail(ATTN_ERR_INVALID_ARG, "head_dim %d < 1", (int)head_dim);
   if (!head_dim_supported(head_dim))
-    return fail(ATTN_ERR_UNSUPPORTED, "no kernel for head_dim %d (supported: 64, 128)",
+    return fail(ATTN_ERR_UNSUPPORTED, "no kernel for head_dim %d (supported: 64, 128, 256)",
                 (int)head_dim);
   if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
   if (sliding_window < 0)

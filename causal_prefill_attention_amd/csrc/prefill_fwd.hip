@@ -55,6 +55,7 @@
 
 #include "device_common.h"
 #include "prefill_params.h"
+#include "prefill_work.h"
 
 namespace attnp {
 namespace {
@@ -92,70 +93,6 @@ struct Cfg {
 };
 
 // ---------------------------------------------------------------- element io
-
-// ------------------------------------------------------------- work decode
-struct Work {
-  int start;   // first query token of the sequence in the packed q / out
-  int len;     // number of queries (new tokens) of the sequence
-  int kstart;  // first key token of the sequence in the packed k / v (unpaged)
-  int klen;    // number of keys: the history followed by the new tokens
-  int q0;      // first local query row of this tile
-  int seq;     // sequence index (the block-table row of a paged cache)
-  bool valid;
-};
-
-// Maps a q-tile slot to (sequence, tile).  Slots enumerate sequences in
-// order; inside a sequence the last (most expensive causal) tile comes
-// first.  Query and key offsets are clamped into [0, T].  Every lane of the
-// wave computes the same answer.  With a paged cache the key count comes
-// from seqlens_k, clamped to the table row's capacity.
-template <int BM, bool PAGED>
-__device__ Work decode_work(const PrefillParams& p, int slot) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int base = 0;
-  for (int s0 = 0; s0 < p.n_seqs; s0 += kWave) {
-    const int s = s0 + lane;
-    int a = 0, b = 0, ka = 0, kb = 0;
-    if (s < p.n_seqs) {
-      a = min(max(p.cu_seqlens[s], 0), p.n_tokens);
-      b = min(max(p.cu_seqlens[s + 1], 0), p.n_tokens);
-      if (PAGED) {
-        kb = min(max(p.seqlens_k[s], 0), p.table_stride * p.page_size);
-      } else {
-        ka = min(max(p.cu_seqlens_k[s], 0), p.n_tokens_k);
-        kb = min(max(p.cu_seqlens_k[s + 1], 0), p.n_tokens_k);
-      }
-    }
-    const int len = max(b - a, 0);
-    const int nt = (len + BM - 1) / BM;
-    int incl = nt;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int y = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += y;
-    }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    if (slot < base + total) {
-      const unsigned long long hit = __ballot(base + incl > slot);
-      const int src = __ffsll((long long)hit) - 1;
-      const int excl = __shfl(incl - nt, src, kWave);
-      Work w;
-      w.start = __shfl(a, src, kWave);
-      w.len = __shfl(len, src, kWave);
-      w.kstart = __shfl(ka, src, kWave);
-      w.klen = __shfl(max(kb - ka, 0), src, kWave);
-      const int ntiles = __shfl(nt, src, kWave);
-      const int rank = slot - base - excl;  // 0 = heaviest tile
-      w.q0 = (ntiles - 1 - rank) * BM;
-      w.seq = s0 + src;
-      w.valid = true;
-      return w;
-    }
-    base += total;
-  }
-  Work w{0, 0, 0, 0, 0, 0, false};
-  return w;
-}
 
 // ------------------------------------------------------------------ kernel
 template <int HDIM, class QT, class KVT, bool PAGED>
@@ -607,7 +544,7 @@ hipError_t launch_dtypes(const PrefillParams& p, DType q_dtype, DType kv_dtype,
 
 }  // namespace
 
-int prefill_min_block_m(int /*head_dim*/) { return kBM; }
+int prefill_min_block_m(int head_dim) { return head_dim == 256 ? prefill_wide_block_m() : kBM; }
 
 int prefill_kv_tile(int /*head_dim*/) { return kBN; }
 
@@ -615,6 +552,7 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
                           DType kv_dtype, hipStream_t stream) {
   if (head_dim == 128) return launch_dtypes<128>(p, q_dtype, kv_dtype, stream);
   if (head_dim == 64) return launch_dtypes<64>(p, q_dtype, kv_dtype, stream);
+  if (head_dim == 256) return launch_prefill_wide(p, head_dim, q_dtype, kv_dtype, stream);
   return hipErrorInvalidValue;
 }
 

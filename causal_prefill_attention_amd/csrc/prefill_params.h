@@ -48,6 +48,11 @@ int prefill_min_block_m(int head_dim);
 // Keys per K/V tile; a paged cache's page_size must be a multiple of it.
 int prefill_kv_tile(int head_dim);
 
+// The wide-head (256-d) prefill kernel: rows per workgroup, and its launcher.
+int prefill_wide_block_m();
+hipError_t launch_prefill_wide(const PrefillParams& p, int head_dim, DType q_dtype,
+                               DType kv_dtype, hipStream_t stream);
+
 // One decode step: one query token per sequence (the sequence's next
 // position) against its keys.  Passed to the decode kernel by value.
 struct DecodeParams {

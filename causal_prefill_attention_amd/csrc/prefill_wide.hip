@@ -1,0 +1,363 @@
+// Causal / sliding-window prefill attention for wide heads (head_dim 256)
+// on gfx950 (CDNA4).  Same operation, inputs, masks and results as the
+// 128-d kernel (causal bound kv_end = min(q_pos + 1, seq_len) of the fused
+// MLA prefill in atlas PR #69; the W most recent keys for a window,
+// m40-llm AGENTS.md "Current Progress"; KV histories and paged caches as
+// in the chunked and paged MLA prefill of atlas PR #69); the head sizes of
+// the HDIM-templated prefill kernels on the atlas page other than 128.
+//
+// Design: a 256-d head needs 128 fp32 accumulator registers and 64 Q
+// operand registers per 32-row wave, more than the two-waves-per-SIMD
+// budget of the 128-d kernel allows.  Here one wave per SIMD (4 waves, 128
+// query rows per workgroup) owns up to 512 registers and runs, per 64-key
+// tile, Sᵀ = K Qᵀ (32 MFMAs), the online softmax and Oᵀ += Vᵀ Pᵀ (32
+// MFMAs); the MFMA chains of one tile overlap the softmax and staging of
+// the wave through the matrix core's queue.  All four waves stage both K
+// (row-major) and Vᵀ (key order of the Sᵀ accumulator) one tile ahead
+// through registers into two LDS stages; one barrier per tile.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "prefill_params.h"
+#include "prefill_work.h"
+
+namespace attnp {
+namespace {
+
+using namespace dev;
+
+constexpr int kXWave = 64;
+constexpr int kXWaves = 4;                 // one per SIMD
+constexpr int kXThreads = kXWave * kXWaves;
+constexpr int kXBN = 64;                   // keys per tile
+constexpr int kXKB = kXBN / 32;
+constexpr int kXKT = kXBN / 16;
+constexpr int kXBM = 32 * kXWaves;         // query rows per workgroup
+constexpr float kXLazy = 8.0f;
+
+template <int HDIM>
+struct WideCfg {
+  static_assert(HDIM % 32 == 0, "head_dim must be a multiple of 32");
+  static constexpr int KSTR = HDIM + 8;
+  static constexpr int VSTR = kXBN + 8;
+  static constexpr int K_ELEMS = kXBN * KSTR;
+  static constexpr int V_ELEMS = HDIM * VSTR;
+  static constexpr int DCH = HDIM / 16;
+  static constexpr int DBLK = HDIM / 32;
+  static constexpr int OCTS = HDIM / 8;
+  static constexpr int K_TOTAL = kXBN * OCTS;
+  static constexpr int V_TOTAL = (kXBN / 4) * OCTS;
+  static constexpr int K_CHUNKS = K_TOTAL / kXThreads;
+  static constexpr int V_UNITS = V_TOTAL / kXThreads;
+  static_assert(K_CHUNKS * kXThreads == K_TOTAL && V_UNITS * kXThreads == V_TOTAL,
+                "every thread stages the same share");
+};
+
+template <int HDIM, class QT, class KVT, bool PAGED>
+__global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParams p) {
+  using C = WideCfg<HDIM>;
+  typedef typename QT::T qelem;
+  typedef typename KVT::T kvelem;
+  constexpr int kStage = 2 * C::K_ELEMS + 2 * C::V_ELEMS;
+  constexpr int kOut = kXWaves * 32 * (HDIM + 8);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kStage > kOut ? kStage : kOut];
+  uint16_t* const kstage0 = smem;
+  uint16_t* const vstage0 = smem + 2 * C::K_ELEMS;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kXWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kXWave);
+  const int slot = blockIdx.x / p.n_q_heads;
+  const int head = blockIdx.x - slot * p.n_q_heads;
+  Work w = decode_work<kXBM, PAGED>(p, slot);
+  if (!w.valid) return;  // uniform across the workgroup
+  w.start = __builtin_amdgcn_readfirstlane(w.start);
+  w.len = __builtin_amdgcn_readfirstlane(w.len);
+  w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
+  w.kstart = __builtin_amdgcn_readfirstlane(w.kstart);
+  w.seq = __builtin_amdgcn_readfirstlane(w.seq);
+  w.klen = __builtin_amdgcn_readfirstlane(w.klen);
+
+  const int kvh = head / p.group;
+  const int hist = w.klen - w.len;  // queries are the last len key positions
+  const int q_end = min(w.len, w.q0 + kXBM);
+  const int kv_hi = min(max(hist + q_end, 0), w.klen);
+  const int kv_lo = p.window > 0 ? min(max(0, hist + w.q0 - p.window + 1), kv_hi) : 0;
+  const int kv_start = kv_lo - kv_lo % kXBN;
+  const int n_tiles = max(1, (kv_hi - kv_start + kXBN - 1) / kXBN);
+
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int wq0 = w.q0 + wave * 32;
+  const int wq_last = min(wq0 + 31, w.len - 1);
+  const bool wave_live = wq0 < w.len;
+  const int myq = wq0 + col;
+  const int mypos = hist + myq;
+
+  // ---- Qᵀ operand: lane holds q[myq, 16c + 8*half .. +7]
+  bf16x8_t qf[C::DCH];
+  {
+    const bool ok = myq < w.len;
+    const qelem* qp = static_cast<const qelem*>(p.q) +
+                      (int64_t)(w.start + (ok ? myq : 0)) * p.q_ts + (int64_t)head * p.q_hs;
+#pragma unroll
+    for (int c = 0; c < C::DCH; ++c) {
+      float f[8];
+      if (ok) {
+        load8f(qp + 16 * c + 8 * half, f);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+      }
+      u32x4_t u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(f[2 * e] * p.q_mult, f[2 * e + 1] * p.q_mult);
+      qf[c] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  }
+
+  // ---- K/V tile movement (every thread stages a share of both)
+  const kvelem* kseq = static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts +
+                       (int64_t)kvh * p.k_hs;
+  const kvelem* vseq = static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts +
+                       (int64_t)kvh * p.v_hs;
+  const int k_row_bytes = (int)(p.k_ts * (int64_t)sizeof(kvelem));
+  const int v_row_bytes = (int)(p.v_ts * (int64_t)sizeof(kvelem));
+  auto tile_slot = [&](int kv0) -> int64_t {
+    if (!PAGED) return kv0;
+    const int* row = p.block_table + (int64_t)w.seq * p.table_stride;
+    const int idx = __builtin_amdgcn_readfirstlane(kv0 / p.page_size);
+    const int page = min(max(row[idx], 0), p.n_pages - 1);
+    return (int64_t)page * p.page_size + (kv0 - idx * p.page_size);
+  };
+  auto rows_of = [&](int kv0) {
+    return __builtin_amdgcn_readfirstlane(max(0, min(kv_hi - kv0, kXBN)));
+  };
+  u32x4_t kst[C::K_CHUNKS];
+  u32x4_t vst[C::V_UNITS][4];
+  auto gload = [&](int kv0) {
+    const int rows = rows_of(kv0);
+    const int64_t slot = tile_slot(kv0);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<kvelem*>(kseq + slot * p.k_ts), 0, rows * k_row_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<kvelem*>(vseq + slot * p.v_ts), 0, rows * v_row_bytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < C::K_CHUNKS; ++i) {
+      const int chunk = tid + i * kXThreads;
+      kst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, (chunk / C::OCTS) * k_row_bytes + 16 * (chunk % C::OCTS), 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < C::V_UNITS; ++u) {
+      const int unit = tid + u * kXThreads;
+      const int kq = unit % (kXBN / 4);
+      const int oct = unit / (kXBN / 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vst[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rv, (4 * kq + i) * v_row_bytes + 16 * oct, 0, 0);
+    }
+  };
+  // K row-major; Vᵀ in the Sᵀ accumulator's key order (inside each 16-key
+  // group, positions 4..7 hold keys 8..11 and positions 8..11 keys 4..7).
+  auto store = [&](int st) {
+    uint16_t* ks = kstage0 + st * C::K_ELEMS;
+    uint16_t* vs = vstage0 + st * C::V_ELEMS;
+#pragma unroll
+    for (int i = 0; i < C::K_CHUNKS; ++i) {
+      const int chunk = tid + i * kXThreads;
+      *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
+          kv_to_bf16(KVT(), kst[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < C::V_UNITS; ++u) {
+      const int unit = tid + u * kXThreads;
+      const int kq = unit % (kXBN / 4);
+      const int oct = unit / (kXBN / 4);
+      const int qq = kq & 3;
+      const int pos = 16 * (kq >> 2) + 4 * (((qq & 1) << 1) | (qq >> 1));
+      u32x4_t r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = kv_to_bf16(KVT(), vst[u][i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x2_t out;
+        out[0] = __builtin_amdgcn_perm(r[1][j >> 1], r[0][j >> 1], sel);
+        out[1] = __builtin_amdgcn_perm(r[3][j >> 1], r[2][j >> 1], sel);
+        *reinterpret_cast<u32x2_t*>(vs + (8 * oct + j) * C::VSTR + pos) = out;
+      }
+    }
+  };
+
+  // ---- per-wave state
+  f32x16_t o[C::DBLK];
+#pragma unroll
+  for (int c = 0; c < C::DBLK; ++c) o[c] = (f32x16_t){};
+  f32x16_t s[kXKB];
+  bf16x8_t pf[kXKT];
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float cmul = p.score_mult;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  auto tile_full = [&](int kv0) {
+    return (kv0 + kXBN - 1 <= hist + wq0) &&
+           (p.window == 0 || kv0 >= hist + wq_last - p.window + 1);
+  };
+  auto scores = [&](int st) {
+    const uint16_t* ks = kstage0 + st * C::K_ELEMS;
+#pragma unroll
+    for (int kb = 0; kb < kXKB; ++kb) s[kb] = (f32x16_t){};
+#pragma unroll
+    for (int c = 0; c < C::DCH; ++c)
+#pragma unroll
+      for (int kb = 0; kb < kXKB; ++kb) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            ks + (32 * kb + col) * C::KSTR + 16 * c + 8 * half);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+      }
+  };
+  auto pv = [&](int st) {
+    const uint16_t* vs = vstage0 + st * C::V_ELEMS;
+#pragma unroll
+    for (int kt = 0; kt < kXKT; ++kt)
+#pragma unroll
+      for (int c = 0; c < C::DBLK; ++c) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            vs + (32 * c + col) * C::VSTR + 16 * kt + 8 * half);
+        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
+      }
+  };
+  auto softmax = [&](int kv0) {
+    if (!tile_full(kv0)) {
+#pragma unroll
+      for (int kb = 0; kb < kXKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key <= mypos && (p.window == 0 || key > mypos - p.window);
+          if (!vis) s[kb][r] = -INFINITY;
+        }
+    }
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < kXKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    mx = pair_max(mx);
+    const bool raise = (mx - m_run) * cmul > kXLazy;
+    const bool any = __ballot(raise) != 0ull;
+    const float m_new = any ? fmaxf(m_run, mx) : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
+    const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
+    m_run = m_new;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < kXKT; ++kt) {
+      u32x4_t u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e], cmul, neg_mc));
+        const float p1 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e + 1], cmul, neg_mc));
+        // (the converted pair feeds the dot product directly; see the 128-d kernel)
+        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        u[e] = __builtin_bit_cast(uint32_t, pb);
+        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
+      }
+      pf[kt] = __builtin_bit_cast(bf16x8_t, u);
+    }
+    l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
+    if (any) {
+#pragma unroll
+      for (int c = 0; c < C::DBLK; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
+    }
+  };
+
+  // ---- tile loop: tile j in stage j & 1, tile j + 1 staged at the end of
+  // iteration j, its loads issued one iteration earlier; one barrier per tile
+  gload(kv_start);
+  store(0);
+  __syncthreads();
+  if (n_tiles > 1) gload(kv_start + kXBN);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int kv0 = kv_start + j * kXBN;
+    scores(j & 1);
+    softmax(kv0);
+    pv(j & 1);
+    if (j + 1 < n_tiles) store((j + 1) & 1);
+    __syncthreads();
+    if (j + 2 < n_tiles) gload(kv0 + 2 * kXBN);
+  }
+
+  // ---- epilogue: O / l -> bf16 via the wave's LDS slice, whole rows stored
+  const float l_tot = pair_sum(l_run);
+  if (wave_live) {
+    constexpr int OSTR = HDIM + 8;
+    uint16_t* ob = smem + wave * 32 * OSTR;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int c = 0; c < C::DBLK; ++c)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        u32x2_t pk;
+        pk[0] = pack_bf16x2(o[c][4 * rb] * inv, o[c][4 * rb + 1] * inv);
+        pk[1] = pack_bf16x2(o[c][4 * rb + 2] * inv, o[c][4 * rb + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(ob + col * OSTR + 32 * c + 8 * rb + 4 * half) = pk;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int CPR = HDIM / 8;
+    constexpr int RPI = kXWave / CPR > 0 ? kXWave / CPR : 1;  // rows per store round
+    constexpr int LPR = CPR / (kXWave / RPI);                  // chunks per lane per row
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + lane / (CPR / LPR);
+#pragma unroll
+      for (int k = 0; k < LPR; ++k) {
+        const int ch = (lane % (CPR / LPR)) * LPR + k;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ob + row * OSTR + 8 * ch);
+        if (wq0 + row < w.len)
+          *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) +
+                                      (int64_t)(w.start + wq0 + row) * p.o_ts +
+                                      (int64_t)head * p.o_hs + 8 * ch) = v;
+      }
+    }
+  }
+}
+
+template <int HDIM, class QT, class KVT>
+hipError_t launch_wide_one(PrefillParams p, hipStream_t stream) {
+  const int64_t slots = (p.n_tokens + kXBM - 1) / kXBM + p.n_seqs;
+  p.tile_slots = (int32_t)slots;
+  const uint64_t blocks = (uint64_t)slots * (uint64_t)p.n_q_heads;
+  if (p.page_size > 0)
+    hipLaunchKernelGGL((prefill_wide_kernel<HDIM, QT, KVT, true>), dim3((uint32_t)blocks),
+                       dim3(kXThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_wide_kernel<HDIM, QT, KVT, false>), dim3((uint32_t)blocks),
+                       dim3(kXThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_wide_block_m() { return kXBM; }
+
+hipError_t launch_prefill_wide(const PrefillParams& p, int head_dim, DType q_dtype,
+                               DType kv_dtype, hipStream_t stream) {
+  if (head_dim != 256) return hipErrorInvalidValue;
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_wide_one<256, BF16, BF16>(p, stream);
+  if (q_dtype == kBF16 && kv_dtype == kFP16) return launch_wide_one<256, BF16, FP16>(p, stream);
+  if (q_dtype == kFP32 && kv_dtype == kBF16) return launch_wide_one<256, FP32, BF16>(p, stream);
+  if (q_dtype == kFP32 && kv_dtype == kFP16) return launch_wide_one<256, FP32, FP16>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attnp

@@ -1,0 +1,80 @@
+// Work decode shared by the prefill kernels: q-tile slot -> (sequence, tile).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "prefill_params.h"
+
+namespace attnp {
+namespace dev {
+
+constexpr int kWorkWave = 64;
+
+// ------------------------------------------------------------- work decode
+struct Work {
+  int start;   // first query token of the sequence in the packed q / out
+  int len;     // number of queries (new tokens) of the sequence
+  int kstart;  // first key token of the sequence in the packed k / v (unpaged)
+  int klen;    // number of keys: the history followed by the new tokens
+  int q0;      // first local query row of this tile
+  int seq;     // sequence index (the block-table row of a paged cache)
+  bool valid;
+};
+
+// Maps a q-tile slot to (sequence, tile).  Slots enumerate sequences in
+// order; inside a sequence the last (most expensive causal) tile comes
+// first.  Query and key offsets are clamped into [0, T].  Every lane of the
+// wave computes the same answer.  With a paged cache the key count comes
+// from seqlens_k, clamped to the table row's capacity.
+template <int BM, bool PAGED>
+__device__ Work decode_work(const PrefillParams& p, int slot) {
+  const int lane = threadIdx.x & (kWorkWave - 1);
+  int base = 0;
+  for (int s0 = 0; s0 < p.n_seqs; s0 += kWorkWave) {
+    const int s = s0 + lane;
+    int a = 0, b = 0, ka = 0, kb = 0;
+    if (s < p.n_seqs) {
+      a = min(max(p.cu_seqlens[s], 0), p.n_tokens);
+      b = min(max(p.cu_seqlens[s + 1], 0), p.n_tokens);
+      if (PAGED) {
+        kb = min(max(p.seqlens_k[s], 0), p.table_stride * p.page_size);
+      } else {
+        ka = min(max(p.cu_seqlens_k[s], 0), p.n_tokens_k);
+        kb = min(max(p.cu_seqlens_k[s + 1], 0), p.n_tokens_k);
+      }
+    }
+    const int len = max(b - a, 0);
+    const int nt = (len + BM - 1) / BM;
+    int incl = nt;
+#pragma unroll
+    for (int off = 1; off < kWorkWave; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWorkWave);
+      if (lane >= off) incl += y;
+    }
+    const int total = __shfl(incl, kWorkWave - 1, kWorkWave);
+    if (slot < base + total) {
+      const unsigned long long hit = __ballot(base + incl > slot);
+      const int src = __ffsll((long long)hit) - 1;
+      const int excl = __shfl(incl - nt, src, kWorkWave);
+      Work w;
+      w.start = __shfl(a, src, kWorkWave);
+      w.len = __shfl(len, src, kWorkWave);
+      w.kstart = __shfl(ka, src, kWorkWave);
+      w.klen = __shfl(max(kb - ka, 0), src, kWorkWave);
+      const int ntiles = __shfl(nt, src, kWorkWave);
+      const int rank = slot - base - excl;  // 0 = heaviest tile
+      w.q0 = (ntiles - 1 - rank) * BM;
+      w.seq = s0 + src;
+      w.valid = true;
+      return w;
+    }
+    base += total;
+  }
+  Work w{0, 0, 0, 0, 0, 0, false};
+  return w;
+}
+
+
+}  // namespace dev
+}  // namespace attnp

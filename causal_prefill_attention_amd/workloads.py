@@ -123,6 +123,10 @@ WORKLOADS: Dict[str, Workload] = {
     "d64_8192tok_32q1kv_outliers": Workload(
         "d64_8192tok_32q1kv_outliers", 7, (8192,), 32, 1, 64,
         k_outlier_frac=0.01, scale=1.0 / 8.0),
+    # 256-d heads, GQA 8:1
+    "d256_4096tok_16q2kv_outliers": Workload(
+        "d256_4096tok_16q2kv_outliers", 10, (4096,), 16, 2, 256,
+        k_outlier_frac=0.01, scale=1.0 / 16.0),
     # decode: 64 sequences of mixed length (512 .. 8191 keys), GQA 4:1
     "decode64_gqa32q8kv_mixed": Workload(
         "decode64_gqa32q8kv_mixed", 8, (1,) * 64, 32, 8, _D, scale=_SCALE,

@@ -40,7 +40,7 @@ def test_status_strings_and_head_dims():
     for code in (B.ATTN_OK, B.ATTN_ERR_INVALID_ARG, B.ATTN_ERR_UNSUPPORTED,
                  B.ATTN_ERR_HIP, 99):
         assert lib.attn_prefill_status_string(code)
-    assert B.supported_head_dims() == [64, 128]
+    assert B.supported_head_dims() == [64, 128, 256]
     assert lib.attn_prefill_version() >= 100
 
 
@@ -85,8 +85,8 @@ BAD = [
     ("zero_kv_heads", lambda a: with_(a, n_kv_heads=0), B.ATTN_ERR_INVALID_ARG, "n_kv_heads"),
     ("heads_not_multiple", lambda a: with_(a, n_q_heads=6, n_kv_heads=4),
      B.ATTN_ERR_INVALID_ARG, "multiple"),
-    ("head_dim_256_unsupported", lambda a: with_(a, head_dim=256),
-     B.ATTN_ERR_UNSUPPORTED, "head_dim 256"),
+    ("head_dim_512_unsupported", lambda a: with_(a, head_dim=512),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 512"),
     ("head_dim_96_unsupported", lambda a: with_(a, head_dim=96),
      B.ATTN_ERR_UNSUPPORTED, "head_dim 96"),
     ("head_dim_zero", lambda a: with_(a, head_dim=0), B.ATTN_ERR_INVALID_ARG, "head_dim"),

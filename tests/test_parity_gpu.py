@@ -646,3 +646,41 @@ def test_decode_strided_views_and_empty_sequence():
     want = oracle.attention_decode(inp["q"], k, v, cu_k, 8, 1, w.attn_scale, 0)
     assert np.all(want[1] == 0.0)
     check("decode_strided", to64(out), want)
+
+
+# ----------------------------------------------------------- head_dim 256
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2)])
+def test_head_dim_256_packed(hq, hkv):
+    w = workloads.custom(f"d256_h{hq}x{hkv}", D64_LENGTHS, hq, hkv, head_dim=256, seed=111)
+    inp = workloads.make_inputs(w)
+    for win in (0, 1, 64, 129):
+        for scale in (1 / 16.0, -0.4):
+            _announce(f"{w.name} W={win} s={scale}")
+            out = run_gpu(inp, hq, hkv, 256, scale, win)
+            check(f"d256_h{hq}x{hkv}_w{win}_s{scale}", to64(out),
+                  oracle_of(inp, hq, hkv, scale, win))
+
+
+@pytest.mark.parametrize("qd,kvd", [("fp32", "fp16"), ("bf16", "fp16")])
+def test_head_dim_256_dtypes(qd, kvd):
+    w = workloads.custom(f"d256_{qd}_{kvd}", [300, 1, 77], 4, 2, head_dim=256, q_dtype=qd,
+                         kv_dtype=kvd, seed=112)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    out = run_gpu(inp, 4, 2, 256, w.attn_scale, 0)
+    check(w.name, to64(out), oracle_of(inp, 4, 2, w.attn_scale, 0))
+
+
+def test_head_dim_256_chunked_and_paged():
+    w = workloads.custom("d256_chunked", [190, 33, 400, 1], 4, 1, head_dim=256, seed=113,
+                         history=[500, 0, 129, 1000])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    for win in (0, 100):
+        out = run_gpu(inp, 4, 1, 256, w.attn_scale, win)
+        check(f"d256_chunked_w{win}", to64(out), oracle_of(inp, 4, 1, w.attn_scale, win))
+    k_pool, v_pool, table = to_paged(inp, 128, seed=12)
+    out = run_paged(inp, k_pool, v_pool, table, 128, 4, 1, w.attn_scale, 0, d=256)
+    want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                  inp["kv_lengths"], 128, 4, 1, w.attn_scale, 0)
+    check("d256_paged", to64(out), want)
