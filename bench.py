@@ -96,7 +96,8 @@ def cpu_baseline(w, inp, n_heads_sample: int):
         oracle.attention_chunked(q, k, v, inp["cu_seqlens"], inp["cu_seqlens_k"], hs,
                                  n_kv, w.attn_scale, w.window, workers=threads)
     dt = time.perf_counter() - t0
-    flops = measure.causal_flops(inp["lengths"], hs, w.head_dim, w.window, kv_lengths)
+    flops = measure.causal_flops(inp["lengths"], hs, w.head_dim, w.window, kv_lengths,
+                                 w.head_dim_v)
     jobs = hs * sum(1 for n in inp["lengths"] if n > 0)
     return {
         "value": flops / dt / 1e12,
@@ -167,12 +168,18 @@ def main():
     cu = inp["cu_seqlens"].to(dev)
     kv_lengths = inp.get("kv_lengths")
     cuk = inp["cu_seqlens_k"].to(dev) if kv_lengths is not None else None
-    out = torch.empty(q.shape[0], w.n_q_heads, w.head_dim, dtype=torch.bfloat16,
-                      device=dev)
+    dv = w.head_dim_v or w.head_dim
+    if w.head_dim_v is not None:
+        v = k[:, :, :w.head_dim_v]  # the values are part of the cache rows
+    out = torch.empty(q.shape[0], w.n_q_heads, dv, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        if w.decode:
+        if w.head_dim_v is not None:
+            binding.attn_prefill_ex(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                    w.head_dim_v, w.attn_scale, w.window,
+                                    cu_seqlens_k=cuk, stream=stream)
+        elif w.decode:
             binding.attn_decode(q, k, v, out, cuk, w.n_q_heads, w.n_kv_heads, w.head_dim,
                                 w.attn_scale, w.window, stream=stream)
         elif cuk is None:
@@ -201,14 +208,16 @@ def main():
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
     avg_ms = sum(durs) / len(durs)
 
-    flops = measure.causal_flops(lengths, w.n_q_heads, w.head_dim, w.window, kv_lengths)
+    flops = measure.causal_flops(lengths, w.n_q_heads, w.head_dim, w.window, kv_lengths,
+                                 w.head_dim_v)
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = measure.PEAK_BF16_TFLOPS
     traffic = load_traffic(name)
     alg_bytes = measure.algorithmic_bytes(lengths, w.n_q_heads, w.n_kv_heads, w.head_dim,
-                                          w.q_dtype, w.kv_dtype, kv_lengths)
+                                          w.q_dtype, w.kv_dtype, kv_lengths, w.head_dim_v,
+                                          v_in_k=w.head_dim_v is not None)
     if w.decode:  # one query per sequence: the step streams K/V from HBM
         roof = {"bound": "hbm", "achieved": round(alg_bytes / (avg_ms * 1e-3) / 1e9, 1),
                 "peak": measure.PEAK_HBM_GBS, "unit": "GB/s"}

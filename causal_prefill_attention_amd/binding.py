@@ -23,7 +23,7 @@ ATTN_FP16 = 1
 ATTN_FP32 = 2
 
 #: Every symbol include/attn_prefill.h declares.
-EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_paged",
+EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_paged", "attn_prefill_ex",
            "attn_decode", "attn_decode_paged", "attn_prefill_status_string",
            "attn_prefill_last_error", "attn_prefill_supported_head_dims",
            "attn_prefill_version")
@@ -84,6 +84,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
         ctypes.POINTER(AttnSeqlens), ctypes.POINTER(AttnPagedKV), ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_prefill_ex.restype = ctypes.c_int
+    lib.attn_prefill_ex.argtypes = [
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
+        ctypes.POINTER(AttnSeqlens), ctypes.POINTER(AttnSeqlens),
+        ctypes.POINTER(AttnPagedKV), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
     lib.attn_decode.restype = ctypes.c_int
     lib.attn_decode.argtypes = [
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
@@ -157,6 +164,21 @@ def call_raw_paged(q: AttnTensor, k_pool: AttnTensor, v_pool: AttnTensor,
         ctypes.byref(q), ctypes.byref(k_pool), ctypes.byref(v_pool), ctypes.byref(out),
         ctypes.byref(seqlens_q), ctypes.byref(paged), int(n_q_heads), int(n_kv_heads),
         int(head_dim), float(scale), int(sliding_window), ctypes.c_void_p(stream))
+
+
+def call_raw_ex(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
+                seqlens_q: AttnSeqlens, seqlens_k: Optional[AttnSeqlens],
+                paged: Optional[AttnPagedKV], n_q_heads: int, n_kv_heads: int,
+                head_dim_qk: int, head_dim_v: int, scale: float, sliding_window: int,
+                stream: Optional[int] = None) -> int:
+    """Calls ``attn_prefill_ex`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_prefill_ex(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(out),
+        ctypes.byref(seqlens_q), ctypes.byref(seqlens_k) if seqlens_k is not None else None,
+        ctypes.byref(paged) if paged is not None else None, int(n_q_heads), int(n_kv_heads),
+        int(head_dim_qk), int(head_dim_v), float(scale), int(sliding_window),
+        ctypes.c_void_p(stream))
 
 
 def call_raw_decode(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
@@ -266,6 +288,22 @@ def attn_prefill_paged(q, k_pool, v_pool, out, cu_seqlens_q, block_table, seqlen
     status = call_raw_paged(describe(q), describe(k_pool), describe(v_pool), describe(out),
                             sq, pg, n_q_heads, n_kv_heads, head_dim, scale,
                             sliding_window, _stream_handle(q, stream))
+    if status != ATTN_OK:
+        raise AttnPrefillError(status, last_error())
+
+
+def attn_prefill_ex(q, k, v, out, cu_seqlens_q, n_q_heads: int, n_kv_heads: int,
+                    head_dim_qk: int, head_dim_v: int, scale: float, sliding_window: int = 0,
+                    cu_seqlens_k=None, stream=None) -> None:
+    """Prefill with separate q/k and v/out head sizes (e.g. 320 / 256, the
+    absorbed MLA layout, where v may be a view of k's first 256 columns);
+    with ``cu_seqlens_k`` the keys carry a history as in
+    ``attn_prefill_chunked``."""
+    sq = _seqlens(cu_seqlens_q, "cu_seqlens_q")
+    sk = _seqlens(cu_seqlens_k, "cu_seqlens_k") if cu_seqlens_k is not None else None
+    status = call_raw_ex(describe(q), describe(k), describe(v), describe(out), sq, sk, None,
+                         n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, scale,
+                         sliding_window, _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
 

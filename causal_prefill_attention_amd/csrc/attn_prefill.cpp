@@ -209,7 +209,8 @@ int debug_validate_paged(const attn_seqlens* cu_q, int64_t n_q, const attn_paged
 int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                 const attn_tensor* out, const attn_seqlens* cu_q, const attn_seqlens* cu_k,
                 const attn_paged_kv* paged, int32_t n_q_heads, int32_t n_kv_heads,
-                int32_t head_dim, float scale, int32_t sliding_window, attn_stream_t stream) {
+                int32_t head_dim, int32_t head_dim_v, float scale, int32_t sliding_window,
+                attn_stream_t stream) {
   g_last_error.clear();
   if (n_q_heads < 1 || n_kv_heads < 1)
     return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
@@ -218,17 +219,22 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
     return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
                 (int)n_q_heads, (int)n_kv_heads);
   if (head_dim < 1) return fail(ATTN_ERR_INVALID_ARG, "head_dim %d < 1", (int)head_dim);
-  if (!head_dim_supported(head_dim))
-    return fail(ATTN_ERR_UNSUPPORTED, "no kernel for head_dim %d (supported: 64, 128, 256)",
-                (int)head_dim);
+  if (head_dim_v < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "head_dim_v %d < 1", (int)head_dim_v);
+  if (head_dim_v == head_dim ? !head_dim_supported(head_dim)
+                             : !(head_dim == 320 && head_dim_v == 256))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "no kernel for head_dim %d / head_dim_v %d (supported: 64, 128 and 256 for "
+                "both, or 320 for q/k with 256 for v/out)",
+                (int)head_dim, (int)head_dim_v);
   if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
   if (sliding_window < 0)
     return fail(ATTN_ERR_INVALID_ARG, "sliding_window %d < 0 (0 = off)", (int)sliding_window);
   int rc;
   if ((rc = check_tensor(q, "q", n_q_heads, head_dim)) != ATTN_OK) return rc;
   if ((rc = check_tensor(k, "k", n_kv_heads, head_dim)) != ATTN_OK) return rc;
-  if ((rc = check_tensor(v, "v", n_kv_heads, head_dim)) != ATTN_OK) return rc;
-  if ((rc = check_tensor(out, "out", n_q_heads, head_dim)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(v, "v", n_kv_heads, head_dim_v)) != ATTN_OK) return rc;
+  if ((rc = check_tensor(out, "out", n_q_heads, head_dim_v)) != ATTN_OK) return rc;
   if (q->dtype != ATTN_BF16 && q->dtype != ATTN_FP32)
     return fail(ATTN_ERR_UNSUPPORTED, "q dtype must be BF16 or FP32");
   if (k->dtype != v->dtype) return fail(ATTN_ERR_UNSUPPORTED, "k and v dtypes differ");
@@ -273,10 +279,10 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
                   t == k ? "k" : "v", (long long)(t->token_stride * elem_bytes(t->dtype)));
   }
   if (T == 0) return ATTN_OK;  // nothing to compute or write
-  const Extent eo = extent_of(out, n_q_heads, head_dim);
+  const Extent eo = extent_of(out, n_q_heads, head_dim_v);
   if (overlaps(eo, extent_of(q, n_q_heads, head_dim)) ||
       overlaps(eo, extent_of(k, n_kv_heads, head_dim)) ||
-      overlaps(eo, extent_of(v, n_kv_heads, head_dim)))
+      overlaps(eo, extent_of(v, n_kv_heads, head_dim_v)))
     return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
 
   const int bm = attnp::prefill_min_block_m(head_dim);
@@ -329,7 +335,7 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
     p.score_mult = fabsf(scale) * log2e;
     p.q_mult = scale < 0.f ? -1.f : 1.f;
   }
-  const hipError_t e = attnp::launch_prefill(p, head_dim, (attnp::DType)q->dtype,
+  const hipError_t e = attnp::launch_prefill(p, head_dim, head_dim_v, (attnp::DType)q->dtype,
                                              (attnp::DType)k->dtype,
                                              reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess)
@@ -528,7 +534,7 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
                  int32_t sliding_window, attn_stream_t stream) {
   return run_prefill(q, k, v, out, cu_seqlens, nullptr, nullptr, n_q_heads, n_kv_heads,
-                     head_dim, scale, sliding_window, stream);
+                     head_dim, head_dim, scale, sliding_window, stream);
 }
 
 int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
@@ -541,7 +547,7 @@ int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k, const attn_
     return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
   }
   return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, nullptr, n_q_heads, n_kv_heads,
-                     head_dim, scale, sliding_window, stream);
+                     head_dim, head_dim, scale, sliding_window, stream);
 }
 
 int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
@@ -554,7 +560,21 @@ int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
     return fail(ATTN_ERR_INVALID_ARG, "paged is NULL");
   }
   return run_prefill(q, k_pool, v_pool, out, cu_seqlens_q, nullptr, paged, n_q_heads,
-                     n_kv_heads, head_dim, scale, sliding_window, stream);
+                     n_kv_heads, head_dim, head_dim, scale, sliding_window, stream);
+}
+
+int attn_prefill_ex(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                    const attn_tensor* out, const attn_seqlens* cu_seqlens_q,
+                    const attn_seqlens* cu_seqlens_k, const attn_paged_kv* paged,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim_qk,
+                    int32_t head_dim_v, float scale, int32_t sliding_window,
+                    attn_stream_t stream) {
+  if (cu_seqlens_k != nullptr && paged != nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k and paged are both set");
+  }
+  return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, paged, n_q_heads, n_kv_heads,
+                     head_dim_qk, head_dim_v, scale, sliding_window, stream);
 }
 
 const char* attn_prefill_status_string(int status) {

@@ -544,15 +544,17 @@ hipError_t launch_dtypes(const PrefillParams& p, DType q_dtype, DType kv_dtype,
 
 }  // namespace
 
-int prefill_min_block_m(int head_dim) { return head_dim == 256 ? prefill_wide_block_m() : kBM; }
+int prefill_min_block_m(int head_dim) { return head_dim >= 256 ? prefill_wide_block_m() : kBM; }
 
 int prefill_kv_tile(int /*head_dim*/) { return kBN; }
 
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
-                          DType kv_dtype, hipStream_t stream) {
-  if (head_dim == 128) return launch_dtypes<128>(p, q_dtype, kv_dtype, stream);
-  if (head_dim == 64) return launch_dtypes<64>(p, q_dtype, kv_dtype, stream);
-  if (head_dim == 256) return launch_prefill_wide(p, head_dim, q_dtype, kv_dtype, stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_dim_qk, int head_dim_v,
+                          DType q_dtype, DType kv_dtype, hipStream_t stream) {
+  if (head_dim_qk == 128 && head_dim_v == 128)
+    return launch_dtypes<128>(p, q_dtype, kv_dtype, stream);
+  if (head_dim_qk == 64 && head_dim_v == 64) return launch_dtypes<64>(p, q_dtype, kv_dtype, stream);
+  if (head_dim_qk >= 256)
+    return launch_prefill_wide(p, head_dim_qk, head_dim_v, q_dtype, kv_dtype, stream);
   return hipErrorInvalidValue;
 }
 

@@ -50,8 +50,8 @@ int prefill_kv_tile(int head_dim);
 
 // The wide-head (256-d) prefill kernel: rows per workgroup, and its launcher.
 int prefill_wide_block_m();
-hipError_t launch_prefill_wide(const PrefillParams& p, int head_dim, DType q_dtype,
-                               DType kv_dtype, hipStream_t stream);
+hipError_t launch_prefill_wide(const PrefillParams& p, int head_dim_qk, int head_dim_v,
+                               DType q_dtype, DType kv_dtype, hipStream_t stream);
 
 // One decode step: one query token per sequence (the sequence's next
 // position) against its keys.  Passed to the decode kernel by value.
@@ -90,7 +90,7 @@ int decode_kv_tile();
 // Launches the kernel for (head_dim, q dtype, kv dtype) on `stream`; picks
 // the workgroup size and sets p.tile_slots.  Returns hipErrorInvalidValue if
 // no instantiation exists.
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, DType q_dtype,
-                          DType kv_dtype, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_dim_qk, int head_dim_v,
+                          DType q_dtype, DType kv_dtype, hipStream_t stream);
 
 }  // namespace attnp

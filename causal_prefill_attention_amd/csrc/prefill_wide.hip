@@ -1,5 +1,8 @@
-// Causal / sliding-window prefill attention for wide heads (head_dim 256)
-// on gfx950 (CDNA4).  Same operation, inputs, masks and results as the
+// Causal / sliding-window prefill attention for wide heads on gfx950
+// (CDNA4): head_dim 256, and q/k head size 320 with v/out head size 256 (the
+// absorbed MLA prefill of atlas PR #69: [q_absorbed | q_rope] against the
+// compressed cache row [kv_latent | k_rope], values = kv_latent, scale
+// 1/sqrt(320)).  Same operation, inputs, masks and results as the
 // 128-d kernel (causal bound kv_end = min(q_pos + 1, seq_len) of the fused
 // MLA prefill in atlas PR #69; the W most recent keys for a window,
 // m40-llm AGENTS.md "Current Progress"; KV histories and paged caches as
@@ -13,8 +16,10 @@
 // tile, Sᵀ = K Qᵀ (32 MFMAs), the online softmax and Oᵀ += Vᵀ Pᵀ (32
 // MFMAs); the MFMA chains of one tile overlap the softmax and staging of
 // the wave through the matrix core's queue.  All four waves stage both K
-// (row-major) and Vᵀ (key order of the Sᵀ accumulator) one tile ahead
-// through registers into two LDS stages; one barrier per tile.
+// (row-major) and Vᵀ (key order of the Sᵀ accumulator) of the next tile
+// through registers into two LDS stages, K and V at different points of the
+// tile so that their staging registers are not live together; one barrier
+// per tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,31 +41,33 @@ constexpr int kXKT = kXBN / 16;
 constexpr int kXBM = 32 * kXWaves;         // query rows per workgroup
 constexpr float kXLazy = 8.0f;
 
-template <int HDIM>
+// DQK: head size of q and k (score contraction), DV: of v and out.
+template <int DQK, int DV>
 struct WideCfg {
-  static_assert(HDIM % 32 == 0, "head_dim must be a multiple of 32");
-  static constexpr int KSTR = HDIM + 8;
+  static_assert(DQK % 16 == 0 && DV % 32 == 0, "head sizes");
+  static constexpr int KSTR = DQK + 8;
   static constexpr int VSTR = kXBN + 8;
   static constexpr int K_ELEMS = kXBN * KSTR;
-  static constexpr int V_ELEMS = HDIM * VSTR;
-  static constexpr int DCH = HDIM / 16;
-  static constexpr int DBLK = HDIM / 32;
-  static constexpr int OCTS = HDIM / 8;
+  static constexpr int V_ELEMS = DV * VSTR;
+  static constexpr int DCH = DQK / 16;
+  static constexpr int DBLK = DV / 32;
+  static constexpr int OCTS = DQK / 8;   // 16-byte chunks per K row
+  static constexpr int VOCTS = DV / 8;   // 16-byte chunks per V row
   static constexpr int K_TOTAL = kXBN * OCTS;
-  static constexpr int V_TOTAL = (kXBN / 4) * OCTS;
+  static constexpr int V_TOTAL = (kXBN / 4) * VOCTS;
   static constexpr int K_CHUNKS = K_TOTAL / kXThreads;
   static constexpr int V_UNITS = V_TOTAL / kXThreads;
   static_assert(K_CHUNKS * kXThreads == K_TOTAL && V_UNITS * kXThreads == V_TOTAL,
                 "every thread stages the same share");
 };
 
-template <int HDIM, class QT, class KVT, bool PAGED>
+template <int DQK, int DV, class QT, class KVT, bool PAGED>
 __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParams p) {
-  using C = WideCfg<HDIM>;
+  using C = WideCfg<DQK, DV>;
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
   constexpr int kStage = 2 * C::K_ELEMS + 2 * C::V_ELEMS;
-  constexpr int kOut = kXWaves * 32 * (HDIM + 8);
+  constexpr int kOut = kXWaves * 32 * (DV + 8);
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStage > kOut ? kStage : kOut];
   uint16_t* const kstage0 = smem;
   uint16_t* const vstage0 = smem + 2 * C::K_ELEMS;
@@ -136,24 +143,26 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   };
   u32x4_t kst[C::K_CHUNKS];
   u32x4_t vst[C::V_UNITS][4];
-  auto gload = [&](int kv0) {
-    const int rows = rows_of(kv0);
-    const int64_t slot = tile_slot(kv0);
+  auto gload_k = [&](int kv0) {
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<kvelem*>(kseq + slot * p.k_ts), 0, rows * k_row_bytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<kvelem*>(vseq + slot * p.v_ts), 0, rows * v_row_bytes, kRsrcWord3);
+        const_cast<kvelem*>(kseq + tile_slot(kv0) * p.k_ts), 0, rows_of(kv0) * k_row_bytes,
+        kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
       const int chunk = tid + i * kXThreads;
       kst[i] = __builtin_amdgcn_raw_buffer_load_b128(
           rk, (chunk / C::OCTS) * k_row_bytes + 16 * (chunk % C::OCTS), 0, 0);
     }
+  };
+  auto gload_v = [&](int kv0) {
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<kvelem*>(vseq + tile_slot(kv0) * p.v_ts), 0, rows_of(kv0) * v_row_bytes,
+        kRsrcWord3);
 #pragma unroll
     for (int u = 0; u < C::V_UNITS; ++u) {
       const int unit = tid + u * kXThreads;
       const int kq = unit % (kXBN / 4);
-      const int oct = unit / (kXBN / 4);
+      const int oct = unit / (kXBN / 4);  // < VOCTS
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         vst[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -162,15 +171,17 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   };
   // K row-major; Vᵀ in the Sᵀ accumulator's key order (inside each 16-key
   // group, positions 4..7 hold keys 8..11 and positions 8..11 keys 4..7).
-  auto store = [&](int st) {
+  auto store_k = [&](int st) {
     uint16_t* ks = kstage0 + st * C::K_ELEMS;
-    uint16_t* vs = vstage0 + st * C::V_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::K_CHUNKS; ++i) {
       const int chunk = tid + i * kXThreads;
       *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
           kv_to_bf16(KVT(), kst[i]);
     }
+  };
+  auto store_v = [&](int st) {
+    uint16_t* vs = vstage0 + st * C::V_ELEMS;
 #pragma unroll
     for (int u = 0; u < C::V_UNITS; ++u) {
       const int unit = tid + u * kXThreads;
@@ -279,26 +290,35 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
     }
   };
 
-  // ---- tile loop: tile j in stage j & 1, tile j + 1 staged at the end of
-  // iteration j, its loads issued one iteration earlier; one barrier per tile
-  gload(kv_start);
-  store(0);
+  // ---- tile loop: tile j in stage j & 1.  Tile j + 1 moves in during
+  // iteration j -- K loaded at its start and stored after the softmax, V
+  // loaded then and stored after P.V -- so the K and V staging registers are
+  // never live at once; stage (j+1) & 1 last held tile j - 1, which every
+  // wave finished before the previous barrier.  One barrier per tile.
+  gload_k(kv_start);
+  gload_v(kv_start);
+  store_k(0);
+  store_v(0);
   __syncthreads();
-  if (n_tiles > 1) gload(kv_start + kXBN);
   for (int j = 0; j < n_tiles; ++j) {
     const int kv0 = kv_start + j * kXBN;
+    const bool more = j + 1 < n_tiles;
+    if (more) gload_k(kv0 + kXBN);
     scores(j & 1);
     softmax(kv0);
+    if (more) {
+      store_k((j + 1) & 1);
+      gload_v(kv0 + kXBN);
+    }
     pv(j & 1);
-    if (j + 1 < n_tiles) store((j + 1) & 1);
+    if (more) store_v((j + 1) & 1);
     __syncthreads();
-    if (j + 2 < n_tiles) gload(kv0 + 2 * kXBN);
   }
 
   // ---- epilogue: O / l -> bf16 via the wave's LDS slice, whole rows stored
   const float l_tot = pair_sum(l_run);
   if (wave_live) {
-    constexpr int OSTR = HDIM + 8;
+    constexpr int OSTR = DV + 8;
     uint16_t* ob = smem + wave * 32 * OSTR;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
@@ -313,7 +333,7 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    constexpr int CPR = HDIM / 8;
+    constexpr int CPR = DV / 8;
     constexpr int RPI = kXWave / CPR > 0 ? kXWave / CPR : 1;  // rows per store round
     constexpr int LPR = CPR / (kXWave / RPI);                  // chunks per lane per row
 #pragma unroll
@@ -332,31 +352,40 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   }
 }
 
-template <int HDIM, class QT, class KVT>
+template <int DQK, int DV, class QT, class KVT>
 hipError_t launch_wide_one(PrefillParams p, hipStream_t stream) {
   const int64_t slots = (p.n_tokens + kXBM - 1) / kXBM + p.n_seqs;
   p.tile_slots = (int32_t)slots;
   const uint64_t blocks = (uint64_t)slots * (uint64_t)p.n_q_heads;
   if (p.page_size > 0)
-    hipLaunchKernelGGL((prefill_wide_kernel<HDIM, QT, KVT, true>), dim3((uint32_t)blocks),
+    hipLaunchKernelGGL((prefill_wide_kernel<DQK, DV, QT, KVT, true>), dim3((uint32_t)blocks),
                        dim3(kXThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_wide_kernel<HDIM, QT, KVT, false>), dim3((uint32_t)blocks),
+    hipLaunchKernelGGL((prefill_wide_kernel<DQK, DV, QT, KVT, false>), dim3((uint32_t)blocks),
                        dim3(kXThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int DQK, int DV>
+hipError_t launch_wide_dtypes(const PrefillParams& p, DType q_dtype, DType kv_dtype,
+                              hipStream_t stream) {
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_wide_one<DQK, DV, BF16, BF16>(p, stream);
+  if (q_dtype == kBF16 && kv_dtype == kFP16) return launch_wide_one<DQK, DV, BF16, FP16>(p, stream);
+  if (q_dtype == kFP32 && kv_dtype == kBF16) return launch_wide_one<DQK, DV, FP32, BF16>(p, stream);
+  if (q_dtype == kFP32 && kv_dtype == kFP16) return launch_wide_one<DQK, DV, FP32, FP16>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int prefill_wide_block_m() { return kXBM; }
 
-hipError_t launch_prefill_wide(const PrefillParams& p, int head_dim, DType q_dtype,
-                               DType kv_dtype, hipStream_t stream) {
-  if (head_dim != 256) return hipErrorInvalidValue;
-  if (q_dtype == kBF16 && kv_dtype == kBF16) return launch_wide_one<256, BF16, BF16>(p, stream);
-  if (q_dtype == kBF16 && kv_dtype == kFP16) return launch_wide_one<256, BF16, FP16>(p, stream);
-  if (q_dtype == kFP32 && kv_dtype == kBF16) return launch_wide_one<256, FP32, BF16>(p, stream);
-  if (q_dtype == kFP32 && kv_dtype == kFP16) return launch_wide_one<256, FP32, FP16>(p, stream);
+hipError_t launch_prefill_wide(const PrefillParams& p, int head_dim_qk, int head_dim_v,
+                               DType q_dtype, DType kv_dtype, hipStream_t stream) {
+  if (head_dim_qk == 256 && head_dim_v == 256)
+    return launch_wide_dtypes<256, 256>(p, q_dtype, kv_dtype, stream);
+  if (head_dim_qk == 320 && head_dim_v == 256)
+    return launch_wide_dtypes<320, 256>(p, q_dtype, kv_dtype, stream);
   return hipErrorInvalidValue;
 }
 

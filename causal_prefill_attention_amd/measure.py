@@ -56,16 +56,24 @@ def visible_pairs(lengths: Sequence[int], window: int,
 
 
 def causal_flops(lengths: Sequence[int], n_q_heads: int, head_dim: int,
-                 window: int, kv_lengths: Optional[Sequence[int]] = None) -> int:
-    return 4 * head_dim * n_q_heads * visible_pairs(lengths, window, kv_lengths)
+                 window: int, kv_lengths: Optional[Sequence[int]] = None,
+                 head_dim_v: Optional[int] = None) -> int:
+    """2 * (d_qk + d_v) flops per visible pair and query head (4 * d when
+    the two head sizes agree)."""
+    dv = head_dim if head_dim_v is None else head_dim_v
+    return 2 * (head_dim + dv) * n_q_heads * visible_pairs(lengths, window, kv_lengths)
 
 
 def algorithmic_bytes(lengths: Sequence[int], n_q_heads: int, n_kv_heads: int,
                       head_dim: int, q_dtype: str, kv_dtype: str,
-                      kv_lengths: Optional[Sequence[int]] = None) -> int:
+                      kv_lengths: Optional[Sequence[int]] = None,
+                      head_dim_v: Optional[int] = None, v_in_k: bool = False) -> int:
+    """Q, K, V read once (V not at all when it is part of K's rows) and the
+    bf16 output written once."""
     t = int(sum(lengths))
     tk = t if kv_lengths is None else int(sum(kv_lengths))
+    dv = head_dim if head_dim_v is None else head_dim_v
     q = t * n_q_heads * head_dim * DTYPE_BYTES[q_dtype]
-    kv = 2 * tk * n_kv_heads * head_dim * DTYPE_BYTES[kv_dtype]
-    o = t * n_q_heads * head_dim * 2
+    kv = tk * n_kv_heads * (head_dim + (0 if v_in_k else dv)) * DTYPE_BYTES[kv_dtype]
+    o = t * n_q_heads * dv * 2
     return q + kv + o

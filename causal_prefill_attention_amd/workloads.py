@@ -62,6 +62,7 @@ class Workload:
     scale: Optional[float] = None  # None -> 1/sqrt(head_dim)
     history: Optional[Tuple[int, ...]] = None  # KV history per sequence (chunked)
     decode: bool = False  # one query per sequence, run through the decode kernel
+    head_dim_v: Optional[int] = None  # v/out head size when it differs (absorbed MLA)
 
     @property
     def attn_scale(self) -> float:
@@ -83,6 +84,7 @@ class Workload:
             "scale": self.attn_scale,
             **({"history": list(self.history)} if self.history else {}),
             **({"decode": True} if self.decode else {}),
+            **({"head_dim_v": self.head_dim_v} if self.head_dim_v else {}),
         }
 
 
@@ -127,6 +129,12 @@ WORKLOADS: Dict[str, Workload] = {
     "d256_4096tok_16q2kv_outliers": Workload(
         "d256_4096tok_16q2kv_outliers", 10, (4096,), 16, 2, 256,
         k_outlier_frac=0.01, scale=1.0 / 16.0),
+    # absorbed MLA prefill: q [q_absorbed | q_rope] (320) against one
+    # compressed cache row [kv_latent | k_rope] (320) per token, v = the
+    # kv_latent part (256), scale 1/sqrt(320)
+    "mla_absorbed_4096tok_16q_320_256": Workload(
+        "mla_absorbed_4096tok_16q_320_256", 11, (4096,), 16, 1, 320,
+        scale=1.0 / math.sqrt(320), head_dim_v=256),
     # decode: 64 sequences of mixed length (512 .. 8191 keys), GQA 4:1
     "decode64_gqa32q8kv_mixed": Workload(
         "decode64_gqa32q8kv_mixed", 8, (1,) * 64, 32, 8, _D, scale=_SCALE,
@@ -207,6 +215,10 @@ def make_inputs(w: Workload) -> Dict[str, object]:
     q = torch.from_numpy(q64).to(_TORCH_DTYPES[w.q_dtype])
     k = torch.from_numpy(k64).to(_TORCH_DTYPES[w.kv_dtype])
     v = torch.from_numpy(v64).to(_TORCH_DTYPES[w.kv_dtype])
+    if w.head_dim_v is not None:
+        # absorbed MLA: the values are the first head_dim_v columns of the
+        # cache row (a view of k); the drawn v is not used
+        v = k[:, :, :w.head_dim_v]
     cu = torch.from_numpy(cu_seqlens_of(lengths))
     out = {
         "q": q, "k": k, "v": v, "cu_seqlens": cu, "lengths": lengths,

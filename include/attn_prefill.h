@@ -175,6 +175,24 @@ int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
                        int32_t n_kv_heads, int32_t head_dim, float scale,
                        int32_t sliding_window, attn_stream_t stream);
 
+/* The general prefill entry point: separate head sizes for the score
+ * contraction (q, k: head_dim_qk) and for the values (v, out: head_dim_v),
+ * with the key layout of attn_prefill (cu_seqlens_k and paged both NULL),
+ * attn_prefill_chunked (cu_seqlens_k set) or attn_prefill_paged (paged
+ * set; both set is ATTN_ERR_INVALID_ARG).  Supported pairs: (64, 64),
+ * (128, 128), (256, 256) and (320, 256), the absorbed MLA prefill of atlas
+ * PR #69 (q = [q_absorbed | q_rope] against the compressed cache row
+ * [kv_latent | k_rope], v = the kv_latent part of the same row -- a view of
+ * k with the same token stride -- and scale 1/sqrt(320)); others are
+ * ATTN_ERR_UNSUPPORTED. */
+int attn_prefill_ex(const attn_tensor* q, const attn_tensor* k,
+                    const attn_tensor* v, const attn_tensor* out,
+                    const attn_seqlens* cu_seqlens_q,
+                    const attn_seqlens* cu_seqlens_k, const attn_paged_kv* paged,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim_qk,
+                    int32_t head_dim_v, float scale, int32_t sliding_window,
+                    attn_stream_t stream);
+
 /* Decode: one new query token per sequence (the batched last-token step).
  * Sequence s's query q[s] sits at position Lk - 1 of its Lk keys and sees
  * all of them (with a window W > 0 the last W).  This is

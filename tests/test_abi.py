@@ -401,3 +401,52 @@ def test_decode_empty_batch_is_a_no_op_without_hip():
         a[key] = mutate(a[key], data=None)
     assert call_decode(**a) == B.ATTN_OK
     assert B.last_error() == ""
+
+
+# ---- attn_prefill_ex: separate head sizes, one key layout
+
+
+def call_ex(a, dqk, dv, seqlens_k=None, paged=None):
+    return B.call_raw_ex(a["q"], a["k"], a["v"], a["out"], a["seqlens"], seqlens_k, paged,
+                         a["n_q_heads"], a["n_kv_heads"], dqk, dv, a["scale"],
+                         a["sliding_window"], None)
+
+
+def ex_args(n=256, hq=8, dqk=320, dv=256):
+    q = tens(FAKE, B.ATTN_BF16, n, hq, dqk)
+    k = tens(FAKE + (1 << 30), B.ATTN_BF16, n, 1, dqk)
+    v = tens(FAKE + (1 << 30), B.ATTN_BF16, n, 1, dv, ts=dqk)  # view of k's first columns
+    o = tens(FAKE + (3 << 30), B.ATTN_BF16, n, hq, dv)
+    s = B.AttnSeqlens(FAKE + (4 << 30), 1, 0)
+    return dict(q=q, k=k, v=v, out=o, seqlens=s, n_q_heads=hq, n_kv_heads=1, head_dim=dqk,
+                scale=1 / math.sqrt(dqk), sliding_window=0)
+
+
+def test_ex_rejects_unsupported_head_pairs():
+    a = ex_args()
+    assert call_ex(a, 320, 128) == B.ATTN_ERR_UNSUPPORTED
+    assert "head_dim 320 / head_dim_v 128" in B.last_error()
+    assert call_ex(a, 512, 512) == B.ATTN_ERR_UNSUPPORTED
+    assert call_ex(a, 320, 0) == B.ATTN_ERR_INVALID_ARG and "head_dim_v" in B.last_error()
+
+
+def test_ex_checks_v_and_out_with_their_own_head_size():
+    a = ex_args()
+    # out described with 256-wide heads but a 200-element head stride overlaps
+    bad = with_(a, out=mutate(a["out"], head_stride=200, token_stride=8 * 256))
+    assert call_ex(bad, 320, 256) == B.ATTN_ERR_INVALID_ARG
+    assert "out: strides" in B.last_error() or "overlap" in B.last_error()
+
+
+def test_ex_rejects_history_and_pages_together():
+    a = ex_args()
+    pg = B.AttnPagedKV(FAKE + (6 << 30), FAKE + (7 << 30), 4, 64)
+    rc = call_ex(a, 320, 256, seqlens_k=B.AttnSeqlens(FAKE, 1, 0), paged=pg)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "both set" in B.last_error()
+
+
+def test_ex_empty_batch_is_a_no_op_without_hip():
+    a = ex_args(n=0)
+    for key in ("q", "k", "v", "out"):
+        a[key] = mutate(a[key], data=None)
+    assert call_ex(a, 320, 256) == B.ATTN_OK

@@ -67,7 +67,12 @@ def run_gpu(inp, hq, hkv, d, scale, window, out=None):
     cu = inp["cu_seqlens"].to(dev)
     if out is None:
         out = torch.empty(q.shape[0], hq, d, dtype=torch.bfloat16, device=dev)
-    if inp.get("decode"):
+    if inp.get("head_dim_v"):
+        out = torch.empty(q.shape[0], hq, inp["head_dim_v"], dtype=torch.bfloat16, device=dev)
+        binding.attn_prefill_ex(q, k, v, out, cu, hq, hkv, d, inp["head_dim_v"], scale, window,
+                                cu_seqlens_k=inp["cu_seqlens_k"].to(dev)
+                                if "cu_seqlens_k" in inp else None)
+    elif inp.get("decode"):
         binding.attn_decode(q, k, v, out, inp["cu_seqlens_k"].to(dev), hq, hkv, d, scale,
                             window)
     elif "cu_seqlens_k" in inp:
@@ -303,6 +308,7 @@ def test_full_size_sampled(name):
     _announce(f"full-size {name}")
     inp = workloads.make_inputs(w)
     inp["decode"] = w.decode
+    inp["head_dim_v"] = w.head_dim_v
     out = run_gpu(inp, w.n_q_heads, w.n_kv_heads, w.head_dim, w.attn_scale, w.window)
     rows = workloads.sample_rows(inp["lengths"], w.n_q_heads, 256, seed=w.seed)
     want = oracle.attention_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
@@ -684,3 +690,59 @@ def test_head_dim_256_chunked_and_paged():
     want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
                                   inp["kv_lengths"], 128, 4, 1, w.attn_scale, 0)
     check("d256_paged", to64(out), want)
+
+
+# ------------------------------------- absorbed MLA: q/k 320, v/out 256
+def mla_inputs(name, lengths, hq, seed, history=None):
+    """q [T, hq, 320]; one compressed cache row [kv_latent(256) | k_rope(64)]
+    per key; k = the row, v = its first 256 columns (a view)."""
+    w = workloads.custom(name, lengths, hq, 1, head_dim=320, seed=seed,
+                         scale=1 / math.sqrt(320), history=history)
+    inp = workloads.make_inputs(w)
+    inp["v"] = inp["k"][:, :, :256]
+    return w, inp
+
+
+def run_mla(inp, hq, window):
+    dev = torch.device("cuda:0")
+    q, c = inp["q"].to(dev), inp["k"].to(dev)
+    out = torch.empty(q.shape[0], hq, 256, dtype=torch.bfloat16, device=dev)
+    binding.attn_prefill_ex(q, c, c[:, :, :256], out, inp["cu_seqlens"].to(dev), hq, 1, 320,
+                            256, 1 / math.sqrt(320), window,
+                            cu_seqlens_k=inp["cu_seqlens_k"].to(dev)
+                            if "cu_seqlens_k" in inp else None)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("win", [0, 1, 100])
+def test_mla_absorbed_320_256_packed(win):
+    w, inp = mla_inputs("mla320", [1000, 1, 129, 0, 300], 8, seed=121)
+    _announce(f"{w.name} W={win}")
+    out = run_mla(inp, 8, win)
+    want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], 8, 1,
+                                   1 / math.sqrt(320), win)
+    check(f"mla320_w{win}", to64(out), want)
+
+
+def test_mla_absorbed_320_256_chunked():
+    w, inp = mla_inputs("mla320_chunked", [200, 64, 1], 16, seed=122,
+                        history=[900, 0, 333])
+    _announce(w.name)
+    out = run_mla(inp, 16, 0)
+    want = oracle.attention_chunked(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                    inp["cu_seqlens_k"], 16, 1, 1 / math.sqrt(320), 0)
+    check("mla320_chunked", to64(out), want)
+
+
+def test_ex_same_head_sizes_match_attn_prefill_bitwise():
+    dev = torch.device("cuda:0")
+    w = workloads.custom("ex_256", [500, 77], 8, 2, head_dim=256, seed=123)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    a = run_gpu(inp, 8, 2, 256, w.attn_scale, 0).clone()
+    b = torch.empty_like(a)
+    binding.attn_prefill_ex(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev), b,
+                            inp["cu_seqlens"].to(dev), 8, 2, 256, 256, w.attn_scale, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
