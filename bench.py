@@ -173,6 +173,9 @@ def main():
         v = k[:, :, :w.head_dim_v]  # the values are part of the cache rows
     out = torch.empty(q.shape[0], w.n_q_heads, dv, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # decode: partial results of key ranges split across workgroups
+    workspace = (binding.decode_workspace(q.shape[0], w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                          device=dev) if w.decode else None)
 
     def step():
         if w.head_dim_v is not None:
@@ -181,7 +184,7 @@ def main():
                                     cu_seqlens_k=cuk, stream=stream)
         elif w.decode:
             binding.attn_decode(q, k, v, out, cuk, w.n_q_heads, w.n_kv_heads, w.head_dim,
-                                w.attn_scale, w.window, stream=stream)
+                                w.attn_scale, w.window, stream=stream, workspace=workspace)
         elif cuk is None:
             binding.attn_prefill(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads,
                                  w.head_dim, w.attn_scale, w.window, stream=stream)

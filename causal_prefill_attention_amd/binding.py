@@ -24,7 +24,8 @@ ATTN_FP32 = 2
 
 #: Every symbol include/attn_prefill.h declares.
 EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_paged", "attn_prefill_ex",
-           "attn_decode", "attn_decode_paged", "attn_prefill_status_string",
+           "attn_decode", "attn_decode_paged", "attn_decode_ws", "attn_decode_paged_ws",
+           "attn_decode_workspace_size", "attn_prefill_status_string",
            "attn_prefill_last_error", "attn_prefill_supported_head_dims",
            "attn_prefill_version")
 
@@ -103,6 +104,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
         ctypes.POINTER(AttnPagedKV), ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_decode_ws.restype = ctypes.c_int
+    lib.attn_decode_ws.argtypes = lib.attn_decode.argtypes[:-1] + [
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_decode_paged_ws.restype = ctypes.c_int
+    lib.attn_decode_paged_ws.argtypes = lib.attn_decode_paged.argtypes[:-1] + [
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32,
+                                               ctypes.c_int32, ctypes.c_int32]
     lib.attn_prefill_status_string.restype = ctypes.c_char_p
     lib.attn_prefill_status_string.argtypes = [ctypes.c_int]
     lib.attn_prefill_last_error.restype = ctypes.c_char_p
@@ -203,6 +213,60 @@ def call_raw_decode_paged(q: AttnTensor, k_pool: AttnTensor, v_pool: AttnTensor,
                                  ctypes.byref(out), ctypes.byref(paged), int(n_q_heads),
                                  int(n_kv_heads), int(head_dim), float(scale),
                                  int(sliding_window), ctypes.c_void_p(stream))
+
+
+def call_raw_decode_ws(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
+                       seqlens_k: AttnSeqlens, n_q_heads: int, n_kv_heads: int,
+                       head_dim: int, scale: float, sliding_window: int,
+                       workspace: Optional[int], workspace_bytes: int,
+                       stream: Optional[int] = None) -> int:
+    """Calls ``attn_decode_ws`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_decode_ws(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                              ctypes.byref(out), ctypes.byref(seqlens_k), int(n_q_heads),
+                              int(n_kv_heads), int(head_dim), float(scale),
+                              int(sliding_window), ctypes.c_void_p(workspace),
+                              int(workspace_bytes), ctypes.c_void_p(stream))
+
+
+def call_raw_decode_paged_ws(q: AttnTensor, k_pool: AttnTensor, v_pool: AttnTensor,
+                             out: AttnTensor, paged: AttnPagedKV, n_q_heads: int,
+                             n_kv_heads: int, head_dim: int, scale: float,
+                             sliding_window: int, workspace: Optional[int],
+                             workspace_bytes: int, stream: Optional[int] = None) -> int:
+    """Calls ``attn_decode_paged_ws`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_decode_paged_ws(ctypes.byref(q), ctypes.byref(k_pool),
+                                    ctypes.byref(v_pool), ctypes.byref(out),
+                                    ctypes.byref(paged), int(n_q_heads), int(n_kv_heads),
+                                    int(head_dim), float(scale), int(sliding_window),
+                                    ctypes.c_void_p(workspace), int(workspace_bytes),
+                                    ctypes.c_void_p(stream))
+
+
+def decode_workspace_size(n_seqs: int, n_q_heads: int, n_kv_heads: int,
+                          head_dim: int) -> int:
+    """Bytes of workspace with which a decode batch uses its preferred split
+    of the keys across workgroups on the current device (0: no split)."""
+    return int(load_library().attn_decode_workspace_size(int(n_seqs), int(n_q_heads),
+                                                         int(n_kv_heads), int(head_dim)))
+
+
+def decode_workspace(n_seqs: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                     device="cuda"):
+    """A workspace tensor (uint8) sized by ``decode_workspace_size``."""
+    import torch
+
+    n = decode_workspace_size(n_seqs, n_q_heads, n_kv_heads, head_dim)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _workspace_ptr(workspace):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def _dtype_code(t) -> int:
@@ -309,21 +373,31 @@ def attn_prefill_ex(q, k, v, out, cu_seqlens_q, n_q_heads: int, n_kv_heads: int,
 
 
 def attn_decode(q, k, v, out, cu_seqlens_k, n_q_heads: int, n_kv_heads: int,
-                head_dim: int, scale: float, sliding_window: int = 0, stream=None) -> None:
+                head_dim: int, scale: float, sliding_window: int = 0, stream=None,
+                workspace=None) -> None:
     """One decode step: q, out [n_seqs, heads, head_dim]; k, v packed by
-    ``cu_seqlens_k`` (each sequence's query sits after its last key)."""
+    ``cu_seqlens_k`` (each sequence's query sits after its last key).  With
+    ``workspace`` (see ``decode_workspace``) a small batch splits each
+    sequence's keys across workgroups (``attn_decode_ws``)."""
     sk = _seqlens(cu_seqlens_k, "cu_seqlens_k")
-    status = call_raw_decode(describe(q), describe(k), describe(v), describe(out), sk,
-                             n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
-                             _stream_handle(q, stream))
+    if workspace is None:
+        status = call_raw_decode(describe(q), describe(k), describe(v), describe(out), sk,
+                                 n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
+                                 _stream_handle(q, stream))
+    else:
+        ptr, nbytes = _workspace_ptr(workspace)
+        status = call_raw_decode_ws(describe(q), describe(k), describe(v), describe(out), sk,
+                                    n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
+                                    ptr, nbytes, _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
 
 
 def attn_decode_paged(q, k_pool, v_pool, out, block_table, seqlens_k, page_size: int,
                       n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
-                      sliding_window: int = 0, stream=None) -> None:
-    """One decode step against a paged K/V cache (see attn_prefill_paged)."""
+                      sliding_window: int = 0, stream=None, workspace=None) -> None:
+    """One decode step against a paged K/V cache (see attn_prefill_paged);
+    ``workspace`` as for ``attn_decode``."""
     import torch
 
     for t, name in ((block_table, "block_table"), (seqlens_k, "seqlens_k")):
@@ -335,9 +409,16 @@ def attn_decode_paged(q, k_pool, v_pool, out, block_table, seqlens_k, page_size:
         raise ValueError("block_table / seqlens_k rows must match the sequences")
     pg = AttnPagedKV(block_table.data_ptr(), seqlens_k.data_ptr(), block_table.shape[1],
                      page_size)
-    status = call_raw_decode_paged(describe(q), describe(k_pool), describe(v_pool),
-                                   describe(out), pg, n_q_heads, n_kv_heads, head_dim,
-                                   scale, sliding_window, _stream_handle(q, stream))
+    if workspace is None:
+        status = call_raw_decode_paged(describe(q), describe(k_pool), describe(v_pool),
+                                       describe(out), pg, n_q_heads, n_kv_heads, head_dim,
+                                       scale, sliding_window, _stream_handle(q, stream))
+    else:
+        ptr, nbytes = _workspace_ptr(workspace)
+        status = call_raw_decode_paged_ws(describe(q), describe(k_pool), describe(v_pool),
+                                          describe(out), pg, n_q_heads, n_kv_heads, head_dim,
+                                          scale, sliding_window, ptr, nbytes,
+                                          _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
 

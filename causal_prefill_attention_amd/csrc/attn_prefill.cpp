@@ -386,11 +386,36 @@ int debug_validate_decode(int64_t n_seqs, const attn_seqlens* cu_k, int64_t Tk,
   return ATTN_OK;
 }
 
-// Both decode entry points: exactly one of cu_k and paged is set.
+// Compute units of the current device (0 if the query fails).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
+}
+
+// Decode work units (sequence, KV head, block of 32 query heads) and the
+// split of each unit's keys that fills about two workgroups per CU.
+int64_t decode_units(int64_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads) {
+  const int64_t group = n_q_heads / n_kv_heads;
+  return n_seqs * n_kv_heads * ((group + 31) / 32);
+}
+int decode_preferred_splits(int64_t units) {
+  const int64_t target = 2 * (int64_t)device_cus();
+  if (units <= 0 || target <= units) return 1;
+  const int64_t s = (target + units - 1) / units;
+  return (int)(s < 32 ? s : 32);
+}
+
+// Both decode entry points: exactly one of cu_k and paged is set; a
+// workspace (may be NULL) lets the keys of a sequence be split across
+// workgroups.
 int run_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                const attn_tensor* out, const attn_seqlens* cu_k, const attn_paged_kv* paged,
                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
-               int32_t sliding_window, attn_stream_t stream) {
+               int32_t sliding_window, void* workspace, size_t workspace_bytes,
+               attn_stream_t stream) {
   g_last_error.clear();
   if (n_q_heads < 1 || n_kv_heads < 1)
     return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
@@ -450,9 +475,28 @@ int run_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
       overlaps(eo, extent_of(v, n_kv_heads, head_dim)))
     return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
   const int64_t group = n_q_heads / n_kv_heads;
-  const int64_t blocks = n_seqs * n_kv_heads * ((group + 31) / 32);
+  if (workspace_bytes > 0 && workspace == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL but workspace_bytes is %zu",
+                workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const int64_t units = decode_units(n_seqs, n_q_heads, n_kv_heads);
+  int n_splits = decode_preferred_splits(units);
+  const int64_t split_bytes = units * (int64_t)attnp::decode_partial_floats(head_dim) * 4;
+  const int64_t fit = split_bytes > 0 ? (int64_t)(workspace_bytes / (size_t)split_bytes) : 0;
+  if (n_splits > fit) n_splits = (int)fit;
+  if (n_splits < 2) n_splits = 1;
+  const int64_t blocks = units * n_splits;
   if (blocks * 256 >= ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)blocks);
+  if (n_splits > 1) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace);
+    const Extent ew = {lo, lo + (uintptr_t)(n_splits * split_bytes)};
+    if (overlaps(ew, eo) || overlaps(ew, extent_of(q, n_q_heads, head_dim)) ||
+        overlaps(ew, extent_of(k, n_kv_heads, head_dim)) ||
+        overlaps(ew, extent_of(v, n_kv_heads, head_dim)))
+      return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps q, k, v or out");
+  }
   const char* dbg = getenv("ATTN_PREFILL_VALIDATE");
   if (dbg != nullptr && dbg[0] == '1') {
     if ((rc = debug_validate_decode(n_seqs, cu_k, Tk, paged, n_pages,
@@ -493,6 +537,8 @@ int run_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
     p.score_mult = fabsf(scale) * log2e;
     p.q_mult = scale < 0.f ? -1.f : 1.f;
   }
+  p.n_splits = n_splits;
+  p.partial = n_splits > 1 ? static_cast<float*>(workspace) : nullptr;
   const hipError_t e = attnp::launch_decode(p, head_dim, (attnp::DType)q->dtype,
                                             (attnp::DType)k->dtype,
                                             reinterpret_cast<hipStream_t>(stream));
@@ -514,7 +560,30 @@ int attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
     return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
   }
   return run_decode(q, k, v, out, cu_seqlens_k, nullptr, n_q_heads, n_kv_heads, head_dim, scale,
-                    sliding_window, stream);
+                    sliding_window, nullptr, 0, stream);
+}
+
+int attn_decode_ws(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                   const attn_tensor* out, const attn_seqlens* cu_seqlens_k, int32_t n_q_heads,
+                   int32_t n_kv_heads, int32_t head_dim, float scale, int32_t sliding_window,
+                   void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  if (cu_seqlens_k == nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
+  }
+  return run_decode(q, k, v, out, cu_seqlens_k, nullptr, n_q_heads, n_kv_heads, head_dim, scale,
+                    sliding_window, workspace, workspace_bytes, stream);
+}
+
+size_t attn_decode_workspace_size(int64_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim) {
+  if (n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 ||
+      head_dim != 128)
+    return 0;
+  const int64_t units = decode_units(n_seqs, n_q_heads, n_kv_heads);
+  const int n_splits = decode_preferred_splits(units);
+  if (n_splits < 2) return 0;
+  return (size_t)(units * n_splits * (int64_t)attnp::decode_partial_floats(head_dim) * 4);
 }
 
 int attn_decode_paged(const attn_tensor* q, const attn_tensor* k_pool, const attn_tensor* v_pool,
@@ -526,7 +595,20 @@ int attn_decode_paged(const attn_tensor* q, const attn_tensor* k_pool, const att
     return fail(ATTN_ERR_INVALID_ARG, "paged is NULL");
   }
   return run_decode(q, k_pool, v_pool, out, nullptr, paged, n_q_heads, n_kv_heads, head_dim,
-                    scale, sliding_window, stream);
+                    scale, sliding_window, nullptr, 0, stream);
+}
+
+int attn_decode_paged_ws(const attn_tensor* q, const attn_tensor* k_pool,
+                         const attn_tensor* v_pool, const attn_tensor* out,
+                         const attn_paged_kv* paged, int32_t n_q_heads, int32_t n_kv_heads,
+                         int32_t head_dim, float scale, int32_t sliding_window, void* workspace,
+                         size_t workspace_bytes, attn_stream_t stream) {
+  if (paged == nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "paged is NULL");
+  }
+  return run_decode(q, k_pool, v_pool, out, nullptr, paged, n_q_heads, n_kv_heads, head_dim,
+                    scale, sliding_window, workspace, workspace_bytes, stream);
 }
 
 int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,

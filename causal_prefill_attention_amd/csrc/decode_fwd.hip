@@ -71,7 +71,8 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   const int half = lane >> 5;
 
   const int hblocks = (p.group + kDHeads - 1) / kDHeads;
-  const int wid = blockIdx.x;
+  const int split = blockIdx.x % p.n_splits;
+  const int wid = blockIdx.x / p.n_splits;
   const int hb = wid % hblocks;
   const int g = (wid / hblocks) % p.n_kv_heads;
   const int s = wid / (hblocks * p.n_kv_heads);
@@ -90,8 +91,11 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   const int kv_lo = p.window > 0 ? max(0, L - p.window) : 0;
   const int kv_start = kv_lo - kv_lo % kDBN;
   const int n_t = L > 0 ? (L - kv_start + kDBN - 1) / kDBN : 0;
-  const int t_begin = __builtin_amdgcn_readfirstlane(wave * n_t / kDWaves);
-  const int t_end = __builtin_amdgcn_readfirstlane((wave + 1) * n_t / kDWaves);
+  // this workgroup's contiguous share of the tiles, then this wave's
+  const int g_begin = split * n_t / p.n_splits;
+  const int g_cnt = (split + 1) * n_t / p.n_splits - g_begin;
+  const int t_begin = __builtin_amdgcn_readfirstlane(g_begin + wave * g_cnt / kDWaves);
+  const int t_end = __builtin_amdgcn_readfirstlane(g_begin + (wave + 1) * g_cnt / kDWaves);
 
   const int hcol = hb * kDHeads + col;     // head index inside the group
   const bool hvalid = hcol < p.group;
@@ -294,6 +298,25 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;  // no visible key: zero row
   const int c = wave;                             // this wave's output block
+  if (p.n_splits > 1) {
+    // unnormalised partial of this split: max (raw score units), sum and
+    // values relative to that max; merged by decode_merge_kernel
+    float* part = p.partial + (int64_t)blockIdx.x * decode_partial_floats(HDIM);
+    if (wave == 0 && half == 0) {
+      part[col] = mx;
+      part[32 + col] = den;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDWaves; ++w)
+        acc += wt[w] * cw[((w * DBLK + c) * 16 + r) * kDWave + lane];
+      const int d = 32 * c + 8 * (r >> 2) + 4 * half + (r & 3);
+      part[64 + d * 32 + col] = acc;
+    }
+    return;
+  }
   if (hvalid) {
     uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)s * p.o_ts + (int64_t)head * p.o_hs;
 #pragma unroll
@@ -315,16 +338,62 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   }
 }
 
+// Merges the n_splits partials of one (sequence, KV head, head block):
+// out = sum_i o_i 2^((m_i - M) c) / sum_i l_i 2^((m_i - M) c), M = max_i m_i.
+template <int HDIM>
+__global__ __launch_bounds__(kDThreads) void decode_merge_kernel(DecodeParams p) {
+  const int hblocks = (p.group + kDHeads - 1) / kDHeads;
+  const int wid = blockIdx.x;
+  const int hb = wid % hblocks;
+  const int g = (wid / hblocks) % p.n_kv_heads;
+  const int s = wid / (hblocks * p.n_kv_heads);
+  const int col = threadIdx.x & 31;
+  const int dg = threadIdx.x >> 5;  // 8 groups of HDIM / 8 values
+  const int hcol = hb * kDHeads + col;
+  if (hcol >= p.group) return;
+  const int head = g * p.group + hcol;
+  const float* base = p.partial + (int64_t)wid * p.n_splits * decode_partial_floats(HDIM);
+  float mx = -INFINITY;
+  for (int i = 0; i < p.n_splits; ++i)
+    mx = fmaxf(mx, base[(int64_t)i * decode_partial_floats(HDIM) + col]);
+  float den = 0.f;
+  for (int i = 0; i < p.n_splits; ++i) {
+    const float* part = base + (int64_t)i * decode_partial_floats(HDIM);
+    const float w = part[col] == -INFINITY ? 0.f : fast_exp2((part[col] - mx) * p.score_mult);
+    den += w * part[32 + col];
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  constexpr int PER = HDIM / 8;
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  for (int i = 0; i < p.n_splits; ++i) {
+    const float* part = base + (int64_t)i * decode_partial_floats(HDIM);
+    const float w = part[col] == -INFINITY ? 0.f : fast_exp2((part[col] - mx) * p.score_mult);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] += w * part[64 + (dg * PER + k) * 32 + col];
+  }
+  uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)s * p.o_ts + (int64_t)head * p.o_hs +
+                 dg * PER;
+#pragma unroll
+  for (int k = 0; k < PER; k += 2)
+    *reinterpret_cast<uint32_t*>(op + k) = pack_bf16x2(acc[k] * inv, acc[k + 1] * inv);
+}
+
 template <class QT, class KVT>
 hipError_t launch_decode_one(const DecodeParams& p, hipStream_t stream) {
   const int64_t hblocks = (p.group + kDHeads - 1) / kDHeads;
-  const uint64_t blocks = (uint64_t)p.n_seqs * (uint64_t)p.n_kv_heads * (uint64_t)hblocks;
+  const uint64_t units = (uint64_t)p.n_seqs * (uint64_t)p.n_kv_heads * (uint64_t)hblocks;
+  const uint64_t blocks = units * (uint64_t)p.n_splits;
   if (p.page_size > 0)
     hipLaunchKernelGGL((decode_fwd_kernel<128, QT, KVT, true>), dim3((uint32_t)blocks),
                        dim3(kDThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((decode_fwd_kernel<128, QT, KVT, false>), dim3((uint32_t)blocks),
                        dim3(kDThreads), 0, stream, p);
+  if (p.n_splits > 1)
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3((uint32_t)units), dim3(kDThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

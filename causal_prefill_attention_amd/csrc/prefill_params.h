@@ -78,7 +78,15 @@ struct DecodeParams {
   int32_t n_pages;
   float score_mult;
   float q_mult;
+  // Split of each sequence's keys across n_splits workgroups (1 = none).
+  // With n_splits > 1 every workgroup writes its unnormalised partial
+  // result to `partial` and a second kernel merges them into out.
+  int32_t n_splits;
+  float* partial;  // [n_seqs][n_kv_heads][hblocks][n_splits][32 + 32 + 32 * d] fp32
 };
+
+// Floats of one split's partial result (max, sum and 32 x head_dim values).
+constexpr int decode_partial_floats(int head_dim) { return 64 + 32 * head_dim; }
 
 // Launches the decode kernel (head_dim 128, q bf16/fp32, kv bf16/fp16).
 hipError_t launch_decode(const DecodeParams& p, int head_dim, DType q_dtype, DType kv_dtype,

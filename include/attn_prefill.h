@@ -54,6 +54,7 @@
 #ifndef ATTN_PREFILL_H
 #define ATTN_PREFILL_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -219,6 +220,41 @@ int attn_decode_paged(const attn_tensor* q, const attn_tensor* k_pool,
                       const attn_paged_kv* paged, int32_t n_q_heads,
                       int32_t n_kv_heads, int32_t head_dim, float scale,
                       int32_t sliding_window, attn_stream_t stream);
+
+/* Decode with a caller-provided workspace.  When a batch has fewer
+ * (sequence, KV head, 32-query-head block) units than about two per compute
+ * unit, each unit's keys are split into up to 32 contiguous ranges computed
+ * by separate workgroups; each writes its running max, softmax denominator
+ * and unnormalised output (fp32) to the workspace, and a second kernel on
+ * the same stream merges the ranges by rescaling each to the common max
+ * (the online-softmax combination used within a kernel, applied across
+ * workgroups).  The result equals attn_decode up to fp32 rounding order.
+ *   workspace: device memory, 16-byte aligned, owned by the caller, not
+ *              read before it is written, not overlapping q, k, v or out;
+ *              may be NULL when workspace_bytes == 0 (then no split: the
+ *              same kernel and result as attn_decode)
+ *   workspace_bytes: its size; the number of ranges is reduced to what
+ *              fits, so any size is valid
+ * Calls that share a workspace on different streams race.  Other arguments
+ * and errors as for attn_decode / attn_decode_paged. */
+int attn_decode_ws(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                   const attn_tensor* out, const attn_seqlens* cu_seqlens_k,
+                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                   float scale, int32_t sliding_window, void* workspace,
+                   size_t workspace_bytes, attn_stream_t stream);
+int attn_decode_paged_ws(const attn_tensor* q, const attn_tensor* k_pool,
+                         const attn_tensor* v_pool, const attn_tensor* out,
+                         const attn_paged_kv* paged, int32_t n_q_heads,
+                         int32_t n_kv_heads, int32_t head_dim, float scale,
+                         int32_t sliding_window, void* workspace,
+                         size_t workspace_bytes, attn_stream_t stream);
+
+/* Workspace bytes with which attn_decode_ws / attn_decode_paged_ws use
+ * their preferred split on the current device for a batch of n_seqs
+ * sequences; 0 when that batch would not be split or the arguments are not
+ * a supported decode shape. */
+size_t attn_decode_workspace_size(int64_t n_seqs, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int32_t head_dim);
 
 /* Static description of a status code (never NULL). */
 const char* attn_prefill_status_string(int status);

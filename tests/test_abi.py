@@ -395,6 +395,49 @@ def test_decode_paged_page_size_checked():
     assert rc == B.ATTN_ERR_UNSUPPORTED and "page_size 32" in B.last_error()
 
 
+def call_decode_ws(workspace, nbytes, **kw):
+    return B.call_raw_decode_ws(kw["q"], kw["k"], kw["v"], kw["out"], kw["seqlens_k"],
+                                kw["n_q_heads"], kw["n_kv_heads"], kw["head_dim"],
+                                kw["scale"], kw["sliding_window"], workspace, nbytes, None)
+
+
+@pytest.mark.parametrize("name,mut,status,frag", BAD_DECODE, ids=[b[0] for b in BAD_DECODE])
+def test_decode_ws_checks_the_same_arguments(name, mut, status, frag):
+    rc = call_decode_ws(FAKE + (8 << 30), 1 << 20, **mut(decode_args()))
+    assert rc == status, (rc, B.last_error())
+    assert frag in B.last_error(), B.last_error()
+
+
+def test_decode_ws_workspace_checked():
+    a = decode_args()
+    rc = call_decode_ws(None, 4096, **a)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "workspace is NULL" in B.last_error()
+    rc = call_decode_ws(FAKE + (8 << 30) + 8, 4096, **a)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "16-byte aligned" in B.last_error()
+    lib = B.load_library()
+    rc = lib.attn_decode_ws(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                            ctypes.byref(a["out"]), None, 32, 8, 128, 0.1, 0, None, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "cu_seqlens_k is NULL" in B.last_error()
+    rc = lib.attn_decode_paged_ws(ctypes.byref(a["q"]), ctypes.byref(a["k"]),
+                                  ctypes.byref(a["v"]), ctypes.byref(a["out"]), None,
+                                  32, 8, 128, 0.1, 0, None, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "paged is NULL" in B.last_error()
+
+
+def test_decode_ws_paged_page_size_checked():
+    a = decode_args()
+    pg = B.AttnPagedKV(FAKE + (6 << 30), FAKE + (7 << 30), 8, 32)
+    rc = B.call_raw_decode_paged_ws(a["q"], a["k"], a["v"], a["out"], pg, 32, 8, 128, 0.1,
+                                    0, FAKE + (8 << 30), 1 << 20, None)
+    assert rc == B.ATTN_ERR_UNSUPPORTED and "page_size 32" in B.last_error()
+
+
+@pytest.mark.parametrize("args", [(0, 32, 1, 128), (4, 32, 1, 64), (4, 30, 8, 128),
+                                  (4, 0, 1, 128), (-1, 32, 1, 128)])
+def test_decode_workspace_size_is_zero_outside_the_contract(args):
+    assert B.decode_workspace_size(*args) == 0
+
+
 def test_decode_empty_batch_is_a_no_op_without_hip():
     a = decode_args(n_seqs=0)
     for key in ("q", "out"):

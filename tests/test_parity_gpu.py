@@ -654,6 +654,97 @@ def test_decode_strided_views_and_empty_sequence():
     check("decode_strided", to64(out), want)
 
 
+# ------------------------------------------------ decode, keys split across workgroups
+def run_decode_ws(inp, hq, hkv, scale, window, workspace):
+    dev = torch.device("cuda:0")
+    out = torch.empty(inp["q"].shape[0], hq, 128, dtype=torch.bfloat16, device=dev)
+    binding.attn_decode(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev), out,
+                        inp["cu_seqlens_k"].to(dev), hq, hkv, 128, scale, window,
+                        workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (8, 2), (40, 8)])
+def test_decode_split_grid(hq, hkv):
+    """A small batch with the preferred split (and with workspaces that fit
+    only a few ranges) against the oracle and against the unsplit kernel."""
+    w, inp = decode_inputs(f"decode_split_h{hq}x{hkv}", DECODE_LENGTHS, hq, hkv, seed=106)
+    n = len(DECODE_LENGTHS)
+    full = binding.decode_workspace_size(n, hq, hkv, 128)
+    assert full > 0, "a batch this small is split"
+    units = n * hkv * ((hq // hkv + 31) // 32)
+    range_bytes = units * (64 + 32 * 128) * 4  # one key range of every unit
+    assert full % range_bytes == 0 and full // range_bytes >= 2
+    for nbytes in (full, 2 * range_bytes + 16, 3 * full):
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")  # NaN floats
+        for win in (0, 1, 64, 300):
+            for scale in (1 / math.sqrt(128), -0.7):
+                _announce(f"{w.name} ws={nbytes} W={win} s={scale:.3f}")
+                out = run_decode_ws(inp, hq, hkv, scale, win, ws)
+                want = oracle.attention_decode(inp["q"], inp["k"], inp["v"],
+                                               inp["cu_seqlens_k"], hq, hkv, scale, win)
+                check(f"decode_split_h{hq}x{hkv}_ws{nbytes}_w{win}_s{scale:.3f}", to64(out),
+                      want)
+                ref = run_gpu(inp, hq, hkv, 128, scale, win)
+                diff = float((out.float() - ref.float()).abs().max())
+                assert diff <= 2e-2, f"split vs unsplit: {diff}"
+
+
+def test_decode_split_long_single_sequence():
+    """One 32K-key sequence (MQA, 32 heads): the case the split exists for."""
+    w, inp = decode_inputs("decode_split_32k", [32768], 32, 1, seed=107)
+    ws = binding.decode_workspace(1, 32, 1, 128)
+    for win in (0, 4096):
+        _announce(f"{w.name} W={win}")
+        out = run_decode_ws(inp, 32, 1, w.attn_scale, win, ws)
+        want = oracle.attention_decode(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_k"],
+                                       32, 1, w.attn_scale, win)
+        check(f"decode_split_32k_w{win}", to64(out), want)
+
+
+def test_decode_split_paged_and_workspace_reuse():
+    """Paged decode with a split, then a smaller batch on the same workspace
+    (stale partials from the first call must not leak into the second)."""
+    w, inp = decode_inputs("decode_split_paged", DECODE_LENGTHS, 32, 2, seed=108)
+    dev = torch.device("cuda:0")
+    ws = binding.decode_workspace(len(DECODE_LENGTHS), 32, 2, 128)
+    k_pool, v_pool, table = to_paged(inp, 64, seed=5)
+    out = torch.empty(len(DECODE_LENGTHS), 32, 128, dtype=torch.bfloat16, device=dev)
+    _announce(w.name)
+    binding.attn_decode_paged(
+        inp["q"].to(dev), k_pool.to(dev), v_pool.to(dev), out, torch.from_numpy(table).to(dev),
+        torch.tensor(inp["kv_lengths"], dtype=torch.int32, device=dev), 64, 32, 2, 128,
+        w.attn_scale, 0, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                  inp["kv_lengths"], 64, 32, 2, w.attn_scale, 0)
+    check("decode_split_paged", to64(out), want)
+    w2, inp2 = decode_inputs("decode_split_reuse", [3000, 17], 32, 2, seed=109)
+    _announce(w2.name)
+    out2 = run_decode_ws(inp2, 32, 2, w2.attn_scale, 0, ws)
+    want2 = oracle.attention_decode(inp2["q"], inp2["k"], inp2["v"], inp2["cu_seqlens_k"],
+                                    32, 2, w2.attn_scale, 0)
+    check("decode_split_reuse", to64(out2), want2)
+
+
+def test_decode_split_full_size_sampled():
+    """The decode benchmark batch (32 sequences of 8192 keys, MQA) with the
+    workspace the benchmark passes, on sampled sequences."""
+    w = workloads.WORKLOADS["decode32_mqa32q1kv_8192"]
+    inp = workloads.make_inputs(w)
+    ws = binding.decode_workspace(32, w.n_q_heads, w.n_kv_heads, 128)
+    _announce(f"{w.name} split")
+    out = to64(run_decode_ws(inp, w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window, ws))
+    cu = inp["cu_seqlens_k"].tolist()
+    for s in (0, 13, 31):
+        sl = slice(cu[s], cu[s + 1])
+        want = oracle.attention_decode(inp["q"][s:s + 1], inp["k"][sl], inp["v"][sl],
+                                       torch.tensor([0, cu[s + 1] - cu[s]], dtype=torch.int32),
+                                       w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window)
+        check(f"{w.name}_split_seq{s}", out[s:s + 1], want)
+
+
 # ----------------------------------------------------------- head_dim 256
 @pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2)])
 def test_head_dim_256_packed(hq, hkv):
