@@ -396,16 +396,18 @@ int device_cus() {
 }
 
 // Decode work units (sequence, KV head, block of 32 query heads) and the
-// split of each unit's keys that fills about two workgroups per CU.
+// split of each unit's keys into ranges: as many as keep every workgroup of
+// the launch resident at once (one per CU: the kernel's LDS admits one), at
+// most kMaxSplits.
 int64_t decode_units(int64_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads) {
   const int64_t group = n_q_heads / n_kv_heads;
   return n_seqs * n_kv_heads * ((group + 31) / 32);
 }
 int decode_preferred_splits(int64_t units) {
-  const int64_t target = 2 * (int64_t)device_cus();
-  if (units <= 0 || target <= units) return 1;
-  const int64_t s = (target + units - 1) / units;
-  return (int)(s < 32 ? s : 32);
+  const int64_t cus = device_cus();
+  if (units <= 0 || 2 * units > cus) return 1;
+  const int64_t s = cus / units;
+  return (int)(s < attnp::kMaxSplits ? s : attnp::kMaxSplits);
 }
 
 // Both decode entry points: exactly one of cu_k and paged is set; a
@@ -486,7 +488,8 @@ int run_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   const int64_t fit = split_bytes > 0 ? (int64_t)(workspace_bytes / (size_t)split_bytes) : 0;
   if (n_splits > fit) n_splits = (int)fit;
   if (n_splits < 2) n_splits = 1;
-  const int64_t blocks = units * n_splits;
+  // the merge kernel of a split batch runs 8 workgroups per unit
+  const int64_t blocks = n_splits > 1 && n_splits < 8 ? units * 8 : units * n_splits;
   if (blocks * 256 >= ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)blocks);
   if (n_splits > 1) {

@@ -101,27 +101,6 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   const bool hvalid = hcol < p.group;
   const int head = g * p.group + (hvalid ? hcol : 0);
 
-  // ---- Qᵀ operand: lane holds q[s, head, 16c + 8*half .. +7] (0 if no head)
-  bf16x8_t qf[DCH];
-  {
-    const qelem* qp = static_cast<const qelem*>(p.q) + (int64_t)s * p.q_ts +
-                      (int64_t)head * p.q_hs;
-#pragma unroll
-    for (int c = 0; c < DCH; ++c) {
-      float f[8];
-      if (hvalid) {
-        load8f(qp + 16 * c + 8 * half, f);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = 0.f;
-      }
-      u32x4_t u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(f[2 * e] * p.q_mult, f[2 * e + 1] * p.q_mult);
-      qf[c] = __builtin_bit_cast(bf16x8_t, u);
-    }
-  }
-
   // ---- tile loads: lane moves chunk (lane % CPR) of rows 4i + lane / CPR
   const kvelem* kbase = static_cast<const kvelem*>(p.k) + (int64_t)g * p.k_hs;
   const kvelem* vbase = static_cast<const kvelem*>(p.v) + (int64_t)g * p.v_hs;
@@ -171,7 +150,29 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   const float cmul = p.score_mult;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+  // first tile in flight before Q, so that the two latencies overlap
   if (t_begin < t_end) gload(kv_start + t_begin * kDBN);
+
+  // ---- Qᵀ operand: lane holds q[s, head, 16c + 8*half .. +7], zeroed for a
+  // column past the group (head is clamped to a real head, so every load is
+  // in bounds and none waits behind a branch)
+  bf16x8_t qf[DCH];
+  {
+    const qelem* qp = static_cast<const qelem*>(p.q) + (int64_t)s * p.q_ts +
+                      (int64_t)head * p.q_hs;
+    const float qm = hvalid ? p.q_mult : 0.f;
+    float f[DCH][8];
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) load8f(qp + 16 * c + 8 * half, f[c]);
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      u32x4_t u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(f[c][2 * e] * qm, f[c][2 * e + 1] * qm);
+      qf[c] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  }
+
   for (int t = t_begin; t < t_end; ++t) {
     const int kv0 = kv_start + t * kDBN;
     lstore();  // tile t: registers -> this wave's LDS slice
@@ -340,44 +341,51 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
 
 // Merges the n_splits partials of one (sequence, KV head, head block):
 // out = sum_i o_i 2^((m_i - M) c) / sum_i l_i 2^((m_i - M) c), M = max_i m_i.
+// Workgroup (unit, slab) handles 16 of the head_dim values of the unit's 32
+// heads: thread (col, pair) reads the split partials of two values, and a
+// wave's 32 columns read 128 contiguous bytes per value.
+constexpr int kMergeSlab = 16;
+
 template <int HDIM>
 __global__ __launch_bounds__(kDThreads) void decode_merge_kernel(DecodeParams p) {
+  constexpr int SLABS = HDIM / kMergeSlab;
+  constexpr int PF = decode_partial_floats(HDIM);
   const int hblocks = (p.group + kDHeads - 1) / kDHeads;
-  const int wid = blockIdx.x;
+  const int wid = blockIdx.x / SLABS;
+  const int slab = blockIdx.x % SLABS;
   const int hb = wid % hblocks;
   const int g = (wid / hblocks) % p.n_kv_heads;
   const int s = wid / (hblocks * p.n_kv_heads);
   const int col = threadIdx.x & 31;
-  const int dg = threadIdx.x >> 5;  // 8 groups of HDIM / 8 values
+  const int d = slab * kMergeSlab + 2 * (threadIdx.x >> 5);
   const int hcol = hb * kDHeads + col;
   if (hcol >= p.group) return;
   const int head = g * p.group + hcol;
-  const float* base = p.partial + (int64_t)wid * p.n_splits * decode_partial_floats(HDIM);
+  const float* base = p.partial + (int64_t)wid * p.n_splits * PF;
+  const int n = p.n_splits;
+  // two rounds of independent loads: every split's max, then its sum and
+  // values (n <= kMaxSplits, so the unrolled loops cover every split)
+  float m[kMaxSplits];
   float mx = -INFINITY;
-  for (int i = 0; i < p.n_splits; ++i)
-    mx = fmaxf(mx, base[(int64_t)i * decode_partial_floats(HDIM) + col]);
-  float den = 0.f;
-  for (int i = 0; i < p.n_splits; ++i) {
-    const float* part = base + (int64_t)i * decode_partial_floats(HDIM);
-    const float w = part[col] == -INFINITY ? 0.f : fast_exp2((part[col] - mx) * p.score_mult);
-    den += w * part[32 + col];
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i) {
+    m[i] = i < n ? base[(int64_t)i * PF + col] : -INFINITY;
+    mx = fmaxf(mx, m[i]);
+  }
+  float den = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxSplits; ++i) {
+    if (i < n) {
+      const float* part = base + (int64_t)i * PF;
+      const float w = m[i] == -INFINITY ? 0.f : fast_exp2((m[i] - mx) * p.score_mult);
+      den += w * part[32 + col];
+      a0 += w * part[64 + d * 32 + col];
+      a1 += w * part[64 + (d + 1) * 32 + col];
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  constexpr int PER = HDIM / 8;
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  for (int i = 0; i < p.n_splits; ++i) {
-    const float* part = base + (int64_t)i * decode_partial_floats(HDIM);
-    const float w = part[col] == -INFINITY ? 0.f : fast_exp2((part[col] - mx) * p.score_mult);
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] += w * part[64 + (dg * PER + k) * 32 + col];
-  }
-  uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)s * p.o_ts + (int64_t)head * p.o_hs +
-                 dg * PER;
-#pragma unroll
-  for (int k = 0; k < PER; k += 2)
-    *reinterpret_cast<uint32_t*>(op + k) = pack_bf16x2(acc[k] * inv, acc[k + 1] * inv);
+  uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)s * p.o_ts + (int64_t)head * p.o_hs;
+  *reinterpret_cast<uint32_t*>(op + d) = pack_bf16x2(a0 * inv, a1 * inv);
 }
 
 template <class QT, class KVT>
@@ -392,8 +400,8 @@ hipError_t launch_decode_one(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((decode_fwd_kernel<128, QT, KVT, false>), dim3((uint32_t)blocks),
                        dim3(kDThreads), 0, stream, p);
   if (p.n_splits > 1)
-    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3((uint32_t)units), dim3(kDThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3((uint32_t)(units * (128 / kMergeSlab))),
+                       dim3(kDThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -87,6 +87,8 @@ struct DecodeParams {
 
 // Floats of one split's partial result (max, sum and 32 x head_dim values).
 constexpr int decode_partial_floats(int head_dim) { return 64 + 32 * head_dim; }
+// Most key ranges one decode unit is split into.
+constexpr int kMaxSplits = 64;
 
 // Launches the decode kernel (head_dim 128, q bf16/fp32, kv bf16/fp16).
 hipError_t launch_decode(const DecodeParams& p, int head_dim, DType q_dtype, DType kv_dtype,

@@ -222,8 +222,8 @@ int attn_decode_paged(const attn_tensor* q, const attn_tensor* k_pool,
                       int32_t sliding_window, attn_stream_t stream);
 
 /* Decode with a caller-provided workspace.  When a batch has fewer
- * (sequence, KV head, 32-query-head block) units than about two per compute
- * unit, each unit's keys are split into up to 32 contiguous ranges computed
+ * (sequence, KV head, 32-query-head block) units than half the compute
+ * units, each unit's keys are split into up to 64 contiguous ranges computed
  * by separate workgroups; each writes its running max, softmax denominator
  * and unnormalised output (fp32) to the workspace, and a second kernel on
  * the same stream merges the ranges by rescaling each to the common max
