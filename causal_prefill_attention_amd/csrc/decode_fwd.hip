@@ -160,17 +160,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   {
     const qelem* qp = static_cast<const qelem*>(p.q) + (int64_t)s * p.q_ts +
                       (int64_t)head * p.q_hs;
-    const float qm = hvalid ? p.q_mult : 0.f;
-    float f[DCH][8];
-#pragma unroll
-    for (int c = 0; c < DCH; ++c) load8f(qp + 16 * c + 8 * half, f[c]);
-#pragma unroll
-    for (int c = 0; c < DCH; ++c) {
-      u32x4_t u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(f[c][2 * e] * qm, f[c][2 * e + 1] * qm);
-      qf[c] = __builtin_bit_cast(bf16x8_t, u);
-    }
+    load_q_operand<DCH>(qp, half, hvalid ? p.q_mult : 0.f, qf);
   }
 
   for (int t = t_begin; t < t_end; ++t) {

@@ -52,6 +52,26 @@ __device__ __forceinline__ void load8f(const float* p, float* f) {
   }
 }
 
+// The Qᵀ MFMA operand of one lane: chunk c holds the eight elements at
+// 16c + 8*half of the query row at qp, times mult (+-1 carries the sign of
+// the scale, 0 blanks a lane without a query; qp must still point at a real
+// row).  Every load is issued before any is used and none sits behind a
+// branch, so the row costs one memory latency.
+template <int DCH, class T>
+__device__ __forceinline__ void load_q_operand(const T* qp, int half, float mult,
+                                               bf16x8_t* qf) {
+  float f[DCH][8];
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) load8f(qp + 16 * c + 8 * half, f[c]);
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) {
+    u32x4_t u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(f[c][2 * e] * mult, f[c][2 * e + 1] * mult);
+    qf[c] = __builtin_bit_cast(bf16x8_t, u);
+  }
+}
+
 // Raw 16-byte K/V chunk -> eight bf16 (identity for bf16 storage).
 __device__ __forceinline__ u32x4_t kv_to_bf16(BF16, u32x4_t raw) { return raw; }
 __device__ __forceinline__ u32x4_t kv_to_bf16(FP16, u32x4_t raw) {

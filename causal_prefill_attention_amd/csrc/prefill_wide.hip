@@ -103,26 +103,11 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   const int mypos = hist + myq;
 
   // ---- Qᵀ operand: lane holds q[myq, 16c + 8*half .. +7]
-  bf16x8_t qf[C::DCH];
-  {
-    const bool ok = myq < w.len;
-    const qelem* qp = static_cast<const qelem*>(p.q) +
-                      (int64_t)(w.start + (ok ? myq : 0)) * p.q_ts + (int64_t)head * p.q_hs;
-#pragma unroll
-    for (int c = 0; c < C::DCH; ++c) {
-      float f[8];
-      if (ok) {
-        load8f(qp + 16 * c + 8 * half, f);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = 0.f;
-      }
-      u32x4_t u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(f[2 * e] * p.q_mult, f[2 * e + 1] * p.q_mult);
-      qf[c] = __builtin_bit_cast(bf16x8_t, u);
-    }
-  }
+  bf16x8_t qf[C::DCH];  // loaded once the first tile's loads are in flight
+  const qelem* const qrow = static_cast<const qelem*>(p.q) +
+                            (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
+                            (int64_t)head * p.q_hs;
+  const float qmul = myq < w.len ? p.q_mult : 0.f;
 
   // ---- K/V tile movement (every thread stages a share of both)
   const kvelem* kseq = static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts +
@@ -297,6 +282,7 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   // wave finished before the previous barrier.  One barrier per tile.
   gload_k(kv_start);
   gload_v(kv_start);
+  load_q_operand<C::DCH>(qrow, half, qmul, qf);
   store_k(0);
   store_v(0);
   __syncthreads();

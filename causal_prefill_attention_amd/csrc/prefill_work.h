@@ -33,17 +33,19 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
   int base = 0;
   for (int s0 = 0; s0 < p.n_seqs; s0 += kWorkWave) {
     const int s = s0 + lane;
-    int a = 0, b = 0, ka = 0, kb = 0;
-    if (s < p.n_seqs) {
-      a = min(max(p.cu_seqlens[s], 0), p.n_tokens);
-      b = min(max(p.cu_seqlens[s + 1], 0), p.n_tokens);
-      if (PAGED) {
-        kb = min(max(p.seqlens_k[s], 0), p.table_stride * p.page_size);
-      } else {
-        ka = min(max(p.cu_seqlens_k[s], 0), p.n_tokens_k);
-        kb = min(max(p.cu_seqlens_k[s + 1], 0), p.n_tokens_k);
-      }
+    // every lane reads a real entry (n_seqs >= 1) with no branch, so the
+    // offsets cost one memory latency; lanes past the batch then drop theirs
+    const int sc = min(s, p.n_seqs - 1);
+    int a = min(max(p.cu_seqlens[sc], 0), p.n_tokens);
+    int b = min(max(p.cu_seqlens[sc + 1], 0), p.n_tokens);
+    int ka = 0, kb;
+    if (PAGED) {
+      kb = min(max(p.seqlens_k[sc], 0), p.table_stride * p.page_size);
+    } else {
+      ka = min(max(p.cu_seqlens_k[sc], 0), p.n_tokens_k);
+      kb = min(max(p.cu_seqlens_k[sc + 1], 0), p.n_tokens_k);
     }
+    if (s >= p.n_seqs) a = b = ka = kb = 0;
     const int len = max(b - a, 0);
     const int nt = (len + BM - 1) / BM;
     int incl = nt;
