@@ -33,7 +33,7 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-const int32_t kHeadDims[] = {64, 128, 256};
+const int32_t kHeadDims[] = {64, 128, 256, 512};
 
 bool head_dim_supported(int32_t d) {
   for (int32_t x : kHeadDims)
@@ -224,8 +224,8 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
   if (head_dim_v == head_dim ? !head_dim_supported(head_dim)
                              : !(head_dim == 320 && head_dim_v == 256))
     return fail(ATTN_ERR_UNSUPPORTED,
-                "no kernel for head_dim %d / head_dim_v %d (supported: 64, 128 and 256 for "
-                "both, or 320 for q/k with 256 for v/out)",
+                "no kernel for head_dim %d / head_dim_v %d (supported: 64, 128, 256 and 512 "
+                "for both, or 320 for q/k with 256 for v/out)",
                 (int)head_dim, (int)head_dim_v);
   if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale is not finite");
   if (sliding_window < 0)

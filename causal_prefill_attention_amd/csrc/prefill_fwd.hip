@@ -531,7 +531,10 @@ hipError_t launch_dtypes(const PrefillParams& p, DType q_dtype, DType kv_dtype,
 
 }  // namespace
 
-int prefill_min_block_m(int head_dim) { return head_dim >= 256 ? prefill_wide_block_m() : kBM; }
+int prefill_min_block_m(int head_dim) {
+  if (head_dim == 512) return prefill_d512_block_m();
+  return head_dim >= 256 ? prefill_wide_block_m() : kBM;
+}
 
 int prefill_kv_tile(int /*head_dim*/) { return kBN; }
 
@@ -540,6 +543,8 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim_qk, int head_dim_
   if (head_dim_qk == 128 && head_dim_v == 128)
     return launch_dtypes<128>(p, q_dtype, kv_dtype, stream);
   if (head_dim_qk == 64 && head_dim_v == 64) return launch_dtypes<64>(p, q_dtype, kv_dtype, stream);
+  if (head_dim_qk == 512 && head_dim_v == 512)
+    return launch_prefill_d512(p, q_dtype, kv_dtype, stream);
   if (head_dim_qk >= 256)
     return launch_prefill_wide(p, head_dim_qk, head_dim_v, q_dtype, kv_dtype, stream);
   return hipErrorInvalidValue;

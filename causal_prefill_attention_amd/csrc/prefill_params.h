@@ -53,6 +53,12 @@ int prefill_wide_block_m();
 hipError_t launch_prefill_wide(const PrefillParams& p, int head_dim_qk, int head_dim_v,
                                DType q_dtype, DType kv_dtype, hipStream_t stream);
 
+// The 512-d prefill kernel (head columns split across the four waves): rows
+// per workgroup, and its launcher.
+int prefill_d512_block_m();
+hipError_t launch_prefill_d512(const PrefillParams& p, DType q_dtype, DType kv_dtype,
+                               hipStream_t stream);
+
 // One decode step: one query token per sequence (the sequence's next
 // position) against its keys.  Passed to the decode kernel by value.
 struct DecodeParams {

@@ -129,6 +129,10 @@ WORKLOADS: Dict[str, Workload] = {
     "d256_4096tok_16q2kv_outliers": Workload(
         "d256_4096tok_16q2kv_outliers", 10, (4096,), 16, 2, 256,
         k_outlier_frac=0.01, scale=1.0 / 16.0),
+    # 512-d heads (the page's path for head sizes above 256), GQA 4:1
+    "d512_4096tok_8q2kv_outliers": Workload(
+        "d512_4096tok_8q2kv_outliers", 12, (4096,), 8, 2, 512,
+        k_outlier_frac=0.01, scale=1.0 / math.sqrt(512)),
     # absorbed MLA prefill: q [q_absorbed | q_rope] (320) against one
     # compressed cache row [kv_latent | k_rope] (320) per token, v = the
     # kv_latent part (256), scale 1/sqrt(320)

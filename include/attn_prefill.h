@@ -105,7 +105,7 @@ typedef struct {
 
 /* Causal (optionally sliding-window) prefill attention, see above.
  *   n_q_heads >= 1, n_kv_heads >= 1, n_q_heads % n_kv_heads == 0
- *   head_dim: one of attn_prefill_supported_head_dims() (64, 128, 256)
+ *   head_dim: one of attn_prefill_supported_head_dims() (64, 128, 256, 512)
  *   scale: finite (0 and negative values allowed), applied to q.k before
  *          masking and softmax
  *   sliding_window: 0 = off, W > 0 = the W most recent keys including the

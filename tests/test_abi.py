@@ -40,7 +40,7 @@ def test_status_strings_and_head_dims():
     for code in (B.ATTN_OK, B.ATTN_ERR_INVALID_ARG, B.ATTN_ERR_UNSUPPORTED,
                  B.ATTN_ERR_HIP, 99):
         assert lib.attn_prefill_status_string(code)
-    assert B.supported_head_dims() == [64, 128, 256]
+    assert B.supported_head_dims() == [64, 128, 256, 512]
     assert lib.attn_prefill_version() >= 100
 
 
@@ -85,8 +85,10 @@ BAD = [
     ("zero_kv_heads", lambda a: with_(a, n_kv_heads=0), B.ATTN_ERR_INVALID_ARG, "n_kv_heads"),
     ("heads_not_multiple", lambda a: with_(a, n_q_heads=6, n_kv_heads=4),
      B.ATTN_ERR_INVALID_ARG, "multiple"),
-    ("head_dim_512_unsupported", lambda a: with_(a, head_dim=512),
-     B.ATTN_ERR_UNSUPPORTED, "head_dim 512"),
+    ("head_dim_1024_unsupported", lambda a: with_(a, head_dim=1024),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 1024"),
+    ("head_dim_384_unsupported", lambda a: with_(a, head_dim=384),
+     B.ATTN_ERR_UNSUPPORTED, "head_dim 384"),
     ("head_dim_96_unsupported", lambda a: with_(a, head_dim=96),
      B.ATTN_ERR_UNSUPPORTED, "head_dim 96"),
     ("head_dim_zero", lambda a: with_(a, head_dim=0), B.ATTN_ERR_INVALID_ARG, "head_dim"),
@@ -469,7 +471,9 @@ def test_ex_rejects_unsupported_head_pairs():
     a = ex_args()
     assert call_ex(a, 320, 128) == B.ATTN_ERR_UNSUPPORTED
     assert "head_dim 320 / head_dim_v 128" in B.last_error()
-    assert call_ex(a, 512, 512) == B.ATTN_ERR_UNSUPPORTED
+    assert call_ex(a, 512, 256) == B.ATTN_ERR_UNSUPPORTED
+    assert "head_dim 512 / head_dim_v 256" in B.last_error()
+    assert call_ex(a, 1024, 1024) == B.ATTN_ERR_UNSUPPORTED
     assert call_ex(a, 320, 0) == B.ATTN_ERR_INVALID_ARG and "head_dim_v" in B.last_error()
 
 
