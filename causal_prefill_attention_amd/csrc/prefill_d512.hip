@@ -24,9 +24,11 @@
 //     r at position (chunk ^ (r & 15)); K operands are read row-wise, Vᵀ
 //     operands with ds_read_b64_tr_b16 (four keys of one column per lane, in
 //     the Sᵀ accumulator's key order).
-//   * Two barriers per tile fence the 32 KiB score exchange; LDS holds four
-//     32 KiB K/V slices plus the exchange, 160 KiB in all.
+//   * Two barriers per tile fence the 32 KiB score exchange (16-byte LDS
+//     writes and reads); LDS holds four 32 KiB K/V slices plus the
+//     exchange, 160 KiB in all.
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 
 #include "device_common.h"
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
 
   // per wave: K slice tile then V slice tile (bf16, rows of 128, swizzled)
   __shared__ __attribute__((aligned(16))) uint16_t kvs[kGWaves * 2 * TILE];
-  // partial scores of every wave: [wave][kb][r][lane]
-  __shared__ __attribute__((aligned(16))) float xch[kGWaves * 2 * 16 * kGWave];
+  // partial scores of every wave: [wave][kb][r / 4][lane] x 4 floats
+  __shared__ __attribute__((aligned(16))) f32x4_t xch[kGWaves * 2 * 4 * kGWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kGWave - 1);
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   float l_run = 0.f;
   const float cmul = p.score_mult;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float* const xw = xch + wave * 2 * 16 * kGWave;
+  f32x4_t* const xw = xch + wave * 2 * 4 * kGWave;
 
   for (int t = 0; t < n_tiles; ++t) {
     const int kv0 = kv_start + t * kGBN;
@@ -183,30 +185,38 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xw[(kb * 16 + r) * kGWave + lane] = sc[kb][r];
+      for (int r4 = 0; r4 < 4; ++r4)
+        xw[(kb * 4 + r4) * kGWave + lane] = (f32x4_t){sc[kb][4 * r4], sc[kb][4 * r4 + 1],
+                                                      sc[kb][4 * r4 + 2], sc[kb][4 * r4 + 3]};
     __syncthreads();
     // full scores, summed in wave order 0..3 in every wave
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = xch[(kb * 16 + r) * kGWave + lane];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4_t acc = xch[(kb * 4 + r4) * kGWave + lane];
 #pragma unroll
-        for (int v = 1; v < kGWaves; ++v) acc += xch[((v * 2 + kb) * 16 + r) * kGWave + lane];
-        sc[kb][r] = acc;
+        for (int v = 1; v < kGWaves; ++v) acc += xch[((v * 2 + kb) * 4 + r4) * kGWave + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[kb][4 * r4 + e] = acc[e];
       }
 
     // mask the causal diagonal, the window start and the key count
     const bool full = (kv0 + kGBN - 1 <= hist + w.q0) &&
                       (p.window == 0 || kv0 >= hist + q_last - p.window + 1);
     if (!full) {
+      // key = kv0 + 4*half + off, off = 32*kb + 8*(r/4) + r%4 (compile-time):
+      // visible when off <= hi and, with a window, off >= lo
+      const int hi = mypos - kv0 - 4 * half;
+      // (lo <= 0 bounds nothing since off >= 0: the subtraction only runs where it
+      // cannot overflow; no branch, the same code with and without a window)
+      const int lo = (p.window > 0 && p.window <= hi) ? hi - p.window + 1 : INT_MIN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key <= mypos && (p.window == 0 || key > mypos - p.window);
-          if (!vis) sc[kb][r] = -INFINITY;
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off > hi || off < lo) sc[kb][r] = -INFINITY;
         }
     }
     // online softmax (lazy max, base 2) into the bf16 Pᵀ operand

@@ -51,6 +51,7 @@
 //     written with another head size's extent (the HDIM=256-on-128 overread
 //     fixed in atlas PR #69).
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 
 #include "device_common.h"
@@ -342,15 +343,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   // the lazy rescale of O and l.
   auto softmax = [&](int kv0) {
     if (!tile_full(kv0)) {
+      // Element r of key block kb holds key kv0 + 4*half + off, with the
+      // compile-time offset off = 32*kb + 8*(r/4) + r%4.  The key is visible
+      // when off <= hi (causal) and, with a window, off >= lo.
+      const int hi = mypos - kv0 - 4 * half;
+      // (lo <= 0 bounds nothing since off >= 0: the subtraction only runs where it
+      // cannot overflow; no branch, the same code with and without a window)
+      const int lo = (p.window > 0 && p.window <= hi) ? hi - p.window + 1 : INT_MIN;
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
+      for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key <= mypos && (p.window == 0 || key > mypos - p.window);
-          if (!vis) s[kb][r] = -INFINITY;
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off > hi || off < lo) s[kb][r] = -INFINITY;
         }
-      }
     }
     // Row max and row sum use four independent partial chains each: with one
     // vector-ALU wave per SIMD in this slot, a single 32-long dependency
