@@ -320,6 +320,100 @@ def test_full_size_sampled(name):
     assert np.all(np.isfinite(got)), "non-finite output somewhere"
 
 
+# ------------------------------------------------------------ size limits
+def test_many_short_sequences_every_kernel():
+    """300 sequences (the work decode scans the offsets 64 at a time, so this
+    takes five passes and carries the tile count across them), empty ones
+    among them, through the 64-, 128-, 256- and 512-wide kernels."""
+    lengths = [int(x) for x in np.random.default_rng(141).integers(0, 41, size=300)]
+    assert 0 in lengths and len(lengths) > 4 * 64
+    for d, hq, hkv in ((128, 4, 2), (64, 2, 1), (256, 2, 1), (512, 2, 1)):
+        w = workloads.custom(f"many_seqs_d{d}", lengths, hq, hkv, head_dim=d, seed=141 + d)
+        inp = workloads.make_inputs(w)
+        for win in (0, 7):
+            _announce(f"{w.name} W={win}")
+            out = run_gpu(inp, hq, hkv, d, w.attn_scale, win)
+            check(f"{w.name}_w{win}", to64(out), oracle_of(inp, hq, hkv, w.attn_scale, win))
+
+
+def test_many_sequences_chunked_and_paged():
+    """150 chunks with histories (the key offsets are scanned with the query
+    offsets), then the same keys through a paged cache."""
+    rng = np.random.default_rng(143)
+    lq = [int(x) for x in rng.integers(0, 21, size=150)]
+    hist = [int(x) for x in rng.integers(0, 101, size=150)]
+    w = workloads.custom("many_chunks", lq, 4, 1, seed=143, history=hist)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    for win in (0, 30):
+        out = run_gpu(inp, 4, 1, 128, w.attn_scale, win)
+        check(f"many_chunks_w{win}", to64(out), oracle_of(inp, 4, 1, w.attn_scale, win))
+    k_pool, v_pool, table = to_paged(inp, 64, seed=14)
+    out = run_paged(inp, k_pool, v_pool, table, 64, 4, 1, w.attn_scale, 0)
+    want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                  inp["kv_lengths"], 64, 4, 1, w.attn_scale, 0)
+    check("many_chunks_paged", to64(out), want)
+
+
+def test_long_sequence_sampled():
+    """One 65,536-token sequence (1024 key tiles for its last query tile),
+    causal and with a 4096-key window, on sampled rows."""
+    w = workloads.custom("long_65536", [65536], 2, 1, seed=144, k_outlier_frac=0.01)
+    inp = workloads.make_inputs(w)
+    rows = workloads.sample_rows(inp["lengths"], 2, 96, seed=144)
+    for win in (0, 4096):
+        _announce(f"{w.name} W={win}")
+        out = to64(run_gpu(inp, 2, 1, 128, w.attn_scale, win))
+        want = oracle.attention_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], 2, 1,
+                                     w.attn_scale, win, rows)
+        check(f"long_65536_w{win}_sampled", np.stack([out[t, h] for t, h in rows]), want)
+        assert np.all(np.isfinite(out))
+
+
+def test_largest_kv_token_stride():
+    """K and V as views with the largest token stride the library accepts
+    (64 strides just under 2 GiB: 16,777,208 bf16 elements per token), for
+    prefill and decode; one element more is rejected on the host."""
+    dev = torch.device("cuda:0")
+    stride = ((1 << 31) - 1) // 64 // 2 // 8 * 8  # elements; a multiple of 16 bytes
+    assert stride * 2 * 64 <= (1 << 31) - 1 < (stride + 8) * 2 * 64
+    lengths = [150, 50]
+    w = workloads.custom("big_stride", lengths, 2, 1, seed=145)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    T = sum(lengths)
+
+    def spread(t):
+        big = torch.empty((T - 1) * stride + 128, dtype=torch.bfloat16, device=dev)
+        view = torch.as_strided(big, (T, 1, 128), (stride, 128, 1))
+        view.copy_(t.to(dev))
+        return big, view
+
+    kb, kview = spread(inp["k"])
+    vb, vview = spread(inp["v"])
+    q = inp["q"].to(dev)
+    cu = inp["cu_seqlens"].to(dev)
+    out = torch.empty(T, 2, 128, dtype=torch.bfloat16, device=dev)
+    binding.attn_prefill(q, kview, vview, out, cu, 2, 1, 128, w.attn_scale, 0)
+    torch.cuda.synchronize()
+    check("big_stride_prefill", to64(out), oracle_of(inp, 2, 1, w.attn_scale, 0))
+    # decode: the last token of each sequence against all of its keys
+    last = [149, 199]
+    dout = torch.empty(2, 2, 128, dtype=torch.bfloat16, device=dev)
+    binding.attn_decode(q[last].contiguous(), kview, vview, dout, cu, 2, 1, 128,
+                        w.attn_scale, 0)
+    torch.cuda.synchronize()
+    check("big_stride_decode", to64(dout), oracle_of(inp, 2, 1, w.attn_scale, 0)[last])
+    too_far = torch.as_strided(kb, (2, 1, 128), (stride + 8, 128, 1))
+    with pytest.raises(binding.AttnPrefillError) as e:
+        binding.attn_prefill(q[:2], too_far, too_far, out[:2],
+                             torch.tensor([0, 2], dtype=torch.int32, device=dev), 2, 1, 128,
+                             w.attn_scale, 0)
+    assert e.value.status == binding.ATTN_ERR_UNSUPPORTED
+    del kb, vb, kview, vview, too_far
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------- chunked prefill against a KV history
 CHUNK_PAIRS = [(1, 1), (1, 200), (2, 2), (63, 64), (64, 64), (65, 300), (128, 1000),
                (200, 200), (0, 50), (257, 258), (3, 700), (256, 256), (255, 1023),
