@@ -28,6 +28,9 @@
 //     normalises and stores one 32-wide block of head_dim.
 //   * Rows of a tile past the key count read as zero through the buffer
 //     range, so padded keys are masked finite values.
+//   * The grid visits the sequences longest first (each workgroup ranks the
+//     batch's tile counts in LDS, up to 256 sequences), so that uneven
+//     lengths do not leave CUs idle at the end.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +50,7 @@ constexpr int kDThreads = kDWave * kDWaves;
 constexpr int kDBN = 64;                   // keys per tile
 constexpr int kDHeads = 32;                // query heads per workgroup (MFMA columns)
 constexpr float kDLazy = 8.0f;             // lazy-max threshold, log2 units
+constexpr int kDSortMax = 256;             // largest batch ranked by length
 
 template <int HDIM, class QT, class KVT, bool PAGED>
 __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p) {
@@ -71,26 +75,67 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   const int half = lane >> 5;
 
   const int hblocks = (p.group + kDHeads - 1) / kDHeads;
+  const int per_seq = hblocks * p.n_kv_heads;  // units of one sequence
   const int split = blockIdx.x % p.n_splits;
-  const int wid = blockIdx.x / p.n_splits;
-  const int hb = wid % hblocks;
-  const int g = (wid / hblocks) % p.n_kv_heads;
-  const int s = wid / (hblocks * p.n_kv_heads);
+  const int order = blockIdx.x / p.n_splits;
+  const int rank = order / per_seq;
+  const int sub = order - rank * per_seq;
+  const int hb = sub % hblocks;
+  const int g = sub / hblocks;
 
-  int kstart = 0, L = 0;
-  if (PAGED) {
-    L = min(max(p.seqlens_k[s], 0), p.table_stride * p.page_size);
-  } else {
-    const int a = min(max(p.cu_seqlens_k[s], 0), p.n_tokens_k);
-    const int b = min(max(p.cu_seqlens_k[s + 1], 0), p.n_tokens_k);
-    kstart = a;
-    L = max(b - a, 0);
+  // keys of sequence i (clamped into the key buffer or the table row) and
+  // the 64-key tiles they take with the window
+  auto seq_keys = [&](int i, int* start) -> int {
+    if (PAGED) {
+      *start = 0;
+      return min(max(p.seqlens_k[i], 0), p.table_stride * p.page_size);
+    }
+    const int a = min(max(p.cu_seqlens_k[i], 0), p.n_tokens_k);
+    const int b = min(max(p.cu_seqlens_k[i + 1], 0), p.n_tokens_k);
+    *start = a;
+    return max(b - a, 0);
+  };
+  auto seq_tiles = [&](int keys) -> int {
+    const int lo = p.window > 0 ? max(0, keys - p.window) : 0;
+    return keys > 0 ? (keys - (lo - lo % kDBN) + kDBN - 1) / kDBN : 0;
+  };
+
+  // ---- longest sequences first.  Units of uneven length taken in
+  // sequence order leave CUs idle at the end (a third of the time for
+  // lengths spread evenly over 512..8191); the grid therefore visits the
+  // sequences in decreasing order of tiles (ties by index) when the batch
+  // is small enough to rank in LDS, else in sequence order.
+  int s = rank;
+  if (p.n_seqs <= kDSortMax) {
+    __shared__ int wts[kDSortMax];
+    __shared__ int pick;
+    for (int i = tid; i < p.n_seqs; i += kDThreads) {
+      int st;
+      wts[i] = seq_tiles(seq_keys(i, &st));
+    }
+    __syncthreads();
+    for (int i = tid; i < p.n_seqs; i += kDThreads) {
+      const int wi = wts[i];
+      int r = 0;
+      for (int j = 0; j < p.n_seqs; ++j) {
+        const int wj = wts[j];
+        r += (wj > wi || (wj == wi && j < i)) ? 1 : 0;
+      }
+      if (r == rank) pick = i;  // ranks are a permutation: exactly one match
+    }
+    __syncthreads();
+    s = pick;
   }
+  s = __builtin_amdgcn_readfirstlane(s);
+  const int unit = s * per_seq + sub;  // the merge kernel's unit numbering
+
+  int kstart = 0;
+  int L = seq_keys(s, &kstart);
   kstart = __builtin_amdgcn_readfirstlane(kstart);
   L = __builtin_amdgcn_readfirstlane(L);
   const int kv_lo = p.window > 0 ? max(0, L - p.window) : 0;
   const int kv_start = kv_lo - kv_lo % kDBN;
-  const int n_t = L > 0 ? (L - kv_start + kDBN - 1) / kDBN : 0;
+  const int n_t = seq_tiles(L);
   // this workgroup's contiguous share of the tiles, then this wave's
   const int g_begin = split * n_t / p.n_splits;
   const int g_cnt = (split + 1) * n_t / p.n_splits - g_begin;
@@ -292,7 +337,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   if (p.n_splits > 1) {
     // unnormalised partial of this split: max (raw score units), sum and
     // values relative to that max; merged by decode_merge_kernel
-    float* part = p.partial + (int64_t)blockIdx.x * decode_partial_floats(HDIM);
+    float* part = p.partial + ((int64_t)unit * p.n_splits + split) * decode_partial_floats(HDIM);
     if (wave == 0 && half == 0) {
       part[col] = mx;
       part[32 + col] = den;
