@@ -173,12 +173,25 @@ def main():
         v = k[:, :, :w.head_dim_v]  # the values are part of the cache rows
     out = torch.empty(q.shape[0], w.n_q_heads, dv, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
-    # decode: partial results of key ranges split across workgroups
-    workspace = (binding.decode_workspace(q.shape[0], w.n_q_heads, w.n_kv_heads, w.head_dim,
-                                          device=dev) if w.decode else None)
+    # partial results of key ranges split across workgroups (decode batches
+    # and prefill calls that would not fill the chip; allocated once, outside
+    # the timed region)
+    workspace = None
+    if w.decode:
+        workspace = binding.decode_workspace(q.shape[0], w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                             device=dev)
+    elif binding.prefill_workspace_size(q.shape[0], k.shape[0], len(lengths), w.n_q_heads,
+                                        w.n_kv_heads, w.head_dim, dv, w.window) > 0:
+        workspace = binding.prefill_workspace(q.shape[0], k.shape[0], len(lengths), w.n_q_heads,
+                                              w.n_kv_heads, w.head_dim, dv, w.window,
+                                              device=dev)
 
     def step():
-        if w.head_dim_v is not None:
+        if workspace is not None and not w.decode:
+            binding.attn_prefill_ex(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads, w.head_dim, dv,
+                                    w.attn_scale, w.window, cu_seqlens_k=cuk, stream=stream,
+                                    workspace=workspace)
+        elif w.head_dim_v is not None:
             binding.attn_prefill_ex(q, k, v, out, cu, w.n_q_heads, w.n_kv_heads, w.head_dim,
                                     w.head_dim_v, w.attn_scale, w.window,
                                     cu_seqlens_k=cuk, stream=stream)
@@ -249,6 +262,8 @@ def main():
             "seq_lens": lengths if len(lengths) <= 16 else f"{len(lengths)} seqs",
             "tokens": int(sum(lengths)),
             **({"kv_history": list(w.history)} if w.history else {}),
+            **({"key_split_workspace_bytes": int(workspace.numel())}
+               if workspace is not None else {}),
             "n_q_heads": w.n_q_heads,
             "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim,

@@ -25,7 +25,8 @@ ATTN_FP32 = 2
 #: Every symbol include/attn_prefill.h declares.
 EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_paged", "attn_prefill_ex",
            "attn_decode", "attn_decode_paged", "attn_decode_ws", "attn_decode_paged_ws",
-           "attn_decode_workspace_size", "attn_prefill_status_string",
+           "attn_decode_workspace_size", "attn_prefill_ex_ws", "attn_prefill_workspace_size",
+           "attn_prefill_status_string",
            "attn_prefill_last_error", "attn_prefill_supported_head_dims",
            "attn_prefill_version")
 
@@ -92,6 +93,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.POINTER(AttnSeqlens), ctypes.POINTER(AttnSeqlens),
         ctypes.POINTER(AttnPagedKV), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.attn_prefill_ex_ws.restype = ctypes.c_int
+    lib.attn_prefill_ex_ws.argtypes = lib.attn_prefill_ex.argtypes[:-1] + [
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.attn_prefill_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32]
     lib.attn_decode.restype = ctypes.c_int
     lib.attn_decode.argtypes = [
         ctypes.POINTER(AttnTensor), ctypes.POINTER(AttnTensor),
@@ -189,6 +197,43 @@ def call_raw_ex(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
         ctypes.byref(paged) if paged is not None else None, int(n_q_heads), int(n_kv_heads),
         int(head_dim_qk), int(head_dim_v), float(scale), int(sliding_window),
         ctypes.c_void_p(stream))
+
+
+def call_raw_ex_ws(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
+                   seqlens_q: AttnSeqlens, seqlens_k: Optional[AttnSeqlens],
+                   paged: Optional[AttnPagedKV], n_q_heads: int, n_kv_heads: int,
+                   head_dim_qk: int, head_dim_v: int, scale: float, sliding_window: int,
+                   workspace: Optional[int], workspace_bytes: int,
+                   stream: Optional[int] = None) -> int:
+    """Calls ``attn_prefill_ex_ws`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_prefill_ex_ws(
+        ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(out),
+        ctypes.byref(seqlens_q), ctypes.byref(seqlens_k) if seqlens_k is not None else None,
+        ctypes.byref(paged) if paged is not None else None, int(n_q_heads), int(n_kv_heads),
+        int(head_dim_qk), int(head_dim_v), float(scale), int(sliding_window),
+        ctypes.c_void_p(workspace), int(workspace_bytes), ctypes.c_void_p(stream))
+
+
+def prefill_workspace_size(n_tokens_q: int, max_keys: int, n_seqs: int, n_q_heads: int,
+                           n_kv_heads: int, head_dim_qk: int, head_dim_v: int,
+                           sliding_window: int = 0) -> int:
+    """Bytes of workspace with which ``attn_prefill_ex_ws`` splits a call on
+    the current device (0: it would not split)."""
+    return int(load_library().attn_prefill_workspace_size(
+        int(n_tokens_q), int(max_keys), int(n_seqs), int(n_q_heads), int(n_kv_heads),
+        int(head_dim_qk), int(head_dim_v), int(sliding_window)))
+
+
+def prefill_workspace(n_tokens_q: int, max_keys: int, n_seqs: int, n_q_heads: int,
+                      n_kv_heads: int, head_dim_qk: int, head_dim_v: int,
+                      sliding_window: int = 0, device="cuda"):
+    """A workspace tensor (uint8) sized by ``prefill_workspace_size``."""
+    import torch
+
+    n = prefill_workspace_size(n_tokens_q, max_keys, n_seqs, n_q_heads, n_kv_heads,
+                               head_dim_qk, head_dim_v, sliding_window)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
 def call_raw_decode(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
@@ -340,15 +385,7 @@ def attn_prefill_paged(q, k_pool, v_pool, out, cu_seqlens_q, block_table, seqlen
     import torch
 
     sq = _seqlens(cu_seqlens_q, "cu_seqlens_q")
-    for t, name in ((block_table, "block_table"), (seqlens_k, "seqlens_k")):
-        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
-    if block_table.dim() != 2 or seqlens_k.dim() != 1:
-        raise ValueError("block_table must be [n_seqs, width], seqlens_k [n_seqs]")
-    if block_table.shape[0] != sq.n_seqs or seqlens_k.shape[0] != sq.n_seqs:
-        raise ValueError("block_table / seqlens_k rows must match the sequences")
-    pg = AttnPagedKV(block_table.data_ptr(), seqlens_k.data_ptr(),
-                     block_table.shape[1], page_size)
+    pg = _paged(block_table, seqlens_k, page_size, sq.n_seqs)
     status = call_raw_paged(describe(q), describe(k_pool), describe(v_pool), describe(out),
                             sq, pg, n_q_heads, n_kv_heads, head_dim, scale,
                             sliding_window, _stream_handle(q, stream))
@@ -358,16 +395,27 @@ def attn_prefill_paged(q, k_pool, v_pool, out, cu_seqlens_q, block_table, seqlen
 
 def attn_prefill_ex(q, k, v, out, cu_seqlens_q, n_q_heads: int, n_kv_heads: int,
                     head_dim_qk: int, head_dim_v: int, scale: float, sliding_window: int = 0,
-                    cu_seqlens_k=None, stream=None) -> None:
+                    cu_seqlens_k=None, stream=None, paged=None, workspace=None) -> None:
     """Prefill with separate q/k and v/out head sizes (e.g. 320 / 256, the
     absorbed MLA layout, where v may be a view of k's first 256 columns);
     with ``cu_seqlens_k`` the keys carry a history as in
-    ``attn_prefill_chunked``."""
+    ``attn_prefill_chunked``; with ``paged = (block_table, seqlens_k,
+    page_size)`` k and v are page pools as in ``attn_prefill_paged``.  With
+    ``workspace`` (see ``prefill_workspace``) a call that would not fill the
+    chip splits each query tile's keys across workgroups
+    (``attn_prefill_ex_ws``)."""
     sq = _seqlens(cu_seqlens_q, "cu_seqlens_q")
     sk = _seqlens(cu_seqlens_k, "cu_seqlens_k") if cu_seqlens_k is not None else None
-    status = call_raw_ex(describe(q), describe(k), describe(v), describe(out), sq, sk, None,
-                         n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, scale,
-                         sliding_window, _stream_handle(q, stream))
+    pg = _paged(*paged, sq.n_seqs) if paged is not None else None
+    if workspace is None:
+        status = call_raw_ex(describe(q), describe(k), describe(v), describe(out), sq, sk, pg,
+                             n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, scale,
+                             sliding_window, _stream_handle(q, stream))
+    else:
+        ptr, nbytes = _workspace_ptr(workspace)
+        status = call_raw_ex_ws(describe(q), describe(k), describe(v), describe(out), sq, sk,
+                                pg, n_q_heads, n_kv_heads, head_dim_qk, head_dim_v, scale,
+                                sliding_window, ptr, nbytes, _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
 
@@ -421,6 +469,20 @@ def attn_decode_paged(q, k_pool, v_pool, out, block_table, seqlens_k, page_size:
                                           _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
+
+
+def _paged(block_table, seqlens_k, page_size: int, n_seqs: int) -> AttnPagedKV:
+    import torch
+
+    for t, name in ((block_table, "block_table"), (seqlens_k, "seqlens_k")):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if block_table.dim() != 2 or seqlens_k.dim() != 1:
+        raise ValueError("block_table must be [n_seqs, width], seqlens_k [n_seqs]")
+    if block_table.shape[0] != n_seqs or seqlens_k.shape[0] != n_seqs:
+        raise ValueError("block_table / seqlens_k rows must match the sequences")
+    return AttnPagedKV(block_table.data_ptr(), seqlens_k.data_ptr(), block_table.shape[1],
+                       page_size)
 
 
 def _seqlens(cu, name: str) -> AttnSeqlens:

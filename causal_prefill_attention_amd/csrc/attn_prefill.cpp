@@ -12,6 +12,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -206,11 +209,126 @@ int debug_validate_paged(const attn_seqlens* cu_q, int64_t n_q, const attn_paged
 // All entry points: cu_k == nullptr and paged == nullptr means the keys are
 // the queries' own tokens (no history); cu_k gives packed keys with a
 // history; paged gives keys in a paged cache.
+// Compute units of the current device (0 if the query fails).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
+}
+
+// Keys of each query tile split across workgroups when the grid would not
+// fill the chip: the 128-d and 64-d kernels only, planned from the shapes
+// the host knows (the offsets stay on the device).  max_keys bounds any
+// sequence's key count.  piece_tiles == 0: no split.
+struct SplitPlan {
+  int32_t piece_tiles = 0;
+  int32_t max_pieces = 1;
+  int64_t bytes = 0;
+};
+
+// Finishing time of workgroups of the given costs on `cus` CUs, taken in
+// grid order (the order the hardware dispatches them), each by the CU that
+// frees up first.
+double list_makespan(const std::vector<double>& jobs, int64_t cus) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int64_t i = 0; i < cus; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (double j : jobs) {
+    const double t = free_at.top() + j;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+SplitPlan plan_prefill_split(int64_t T, int64_t max_keys, int64_t n_seqs, int32_t n_q_heads,
+                             int32_t head_dim, int32_t head_dim_v, int32_t window) {
+  SplitPlan sp;
+  if (head_dim != head_dim_v || (head_dim != 128 && head_dim != 64) || T <= 0) return sp;
+  const int64_t bm = attnp::prefill_min_block_m(head_dim);
+  const int64_t tile = attnp::prefill_kv_tile(head_dim);
+  const int64_t slots = (T + bm - 1) / bm + n_seqs;
+  const int64_t grid = slots * n_q_heads;
+  const int64_t cus = device_cus();
+  if (cus <= 0 || grid >= 2 * cus) return sp;  // enough workgroups already
+  const int64_t max_nt = (max_keys + tile - 1) / tile + 1;  // +1: window alignment
+  auto finish = [&](int32_t c, int64_t pieces) {
+    sp.piece_tiles = c;
+    sp.max_pieces = (int32_t)pieces;
+    sp.bytes = slots * pieces * n_q_heads * attnp::prefill_partial_floats(head_dim, (int)bm) * 4;
+    return sp;
+  };
+  if (n_seqs == 1 && T <= max_keys && grid <= 16384) {
+    // One sequence: every query tile's key tiles are known (the keys are a
+    // history of max_keys - T followed by the T queries).  Compare the
+    // finishing time of whole tiles with that of pieces, both in grid order
+    // (heaviest query tile first, its pieces next, heads innermost), in
+    // units of one key tile's time: 2.5 more per workgroup (prologue and
+    // epilogue), 12 more per piece of a split tile (a CU's share of HBM
+    // time to write its fp32 partial and read it back in the merge) and 0.5
+    // per empty grid piece.  Measured: 4 query heads over 8192 tokens run
+    // fastest with 48-tile pieces at half the unsplit time, and 2048 tokens
+    // over 32 heads run slower with any split; the model gives both.
+    const int64_t hist = max_keys - T;
+    std::vector<int64_t> nts;  // grid order: the last query tile first
+    for (int64_t q0 = ((T - 1) / bm) * bm; q0 >= 0; q0 -= bm) {
+      const int64_t kv_hi = hist + std::min(T, q0 + bm);
+      const int64_t kv_lo = window > 0 ? std::max<int64_t>(0, hist + q0 - window + 1) : 0;
+      nts.push_back(std::max<int64_t>(1, (kv_hi - (kv_lo - kv_lo % tile) + tile - 1) / tile));
+    }
+    std::vector<double> jobs;
+    for (int64_t nt : nts)
+      for (int32_t h = 0; h < n_q_heads; ++h) jobs.push_back((double)nt + 2.5);
+    const double whole = list_makespan(jobs, cus);
+    double best = 0.85 * whole;  // split only for a clear gain
+    int32_t best_c = 0;
+    int64_t best_mp = 1;
+    for (int32_t c : {4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128}) {
+      int64_t mp = 1, n_jobs = 0;
+      for (int64_t nt : nts) {
+        mp = std::max(mp, (nt + c - 1) / c);
+        n_jobs += (nt + c - 1) / c * n_q_heads;
+      }
+      if (mp < 2) break;                // no tile is split at this length or above
+      if (n_jobs > 16 * cus) continue;  // pieces this short cost more than they save
+      jobs.clear();
+      for (int64_t nt : nts) {
+        const int64_t n = (nt + c - 1) / c;
+        for (int64_t i = 0; i < mp; ++i)
+          for (int32_t h = 0; h < n_q_heads; ++h)
+            jobs.push_back(i >= n ? 0.5
+                                  : (double)std::min<int64_t>(c, nt - i * c) + 2.5 +
+                                        (n > 1 ? 12.0 : 0.0));
+      }
+      const double t = list_makespan(jobs, cus);
+      if (t < best) {
+        best = t;
+        best_c = c;
+        best_mp = mp;
+      }
+    }
+    if (best_c == 0) return sp;
+    return finish(best_c, best_mp);
+  }
+  // Several sequences (lengths unknown here): split only a grid with fewer
+  // workgroups than CUs, into about two pieces per query tile on average.
+  if (grid >= cus) return sp;
+  const int64_t want = (2 * cus + grid - 1) / grid;
+  int64_t c = (max_nt + 2 * want - 1) / (2 * want);
+  if (c < 8) c = 8;
+  const int64_t pieces = (max_nt + c - 1) / c;
+  if (pieces < 2 || c > INT32_MAX) return sp;
+  return finish((int32_t)c, pieces);
+}
+
 int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                 const attn_tensor* out, const attn_seqlens* cu_q, const attn_seqlens* cu_k,
                 const attn_paged_kv* paged, int32_t n_q_heads, int32_t n_kv_heads,
                 int32_t head_dim, int32_t head_dim_v, float scale, int32_t sliding_window,
-                attn_stream_t stream) {
+                void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   g_last_error.clear();
   if (n_q_heads < 1 || n_kv_heads < 1)
     return fail(ATTN_ERR_INVALID_ARG, "n_q_heads (%d) and n_kv_heads (%d) must be >= 1",
@@ -285,9 +403,31 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
       overlaps(eo, extent_of(v, n_kv_heads, head_dim_v)))
     return fail(ATTN_ERR_INVALID_ARG, "out overlaps q, k or v");
 
+  if (workspace_bytes > 0 && workspace == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace is NULL but workspace_bytes is %zu",
+                workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  SplitPlan sp;
+  if (workspace_bytes > 0) {
+    const int64_t max_keys =
+        paged != nullptr ? (int64_t)paged->table_stride * paged->page_size : Tk;
+    sp = plan_prefill_split(T, max_keys, cu_q->n_seqs, n_q_heads, head_dim, head_dim_v,
+                            sliding_window);
+    if (sp.bytes > (int64_t)workspace_bytes) sp = SplitPlan();  // too small: no split
+  }
+  if (sp.piece_tiles > 0) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace);
+    const Extent ew = {lo, lo + (uintptr_t)sp.bytes};
+    if (overlaps(ew, eo) || overlaps(ew, extent_of(q, n_q_heads, head_dim)) ||
+        overlaps(ew, extent_of(k, n_kv_heads, head_dim)) ||
+        overlaps(ew, extent_of(v, n_kv_heads, head_dim_v)))
+      return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps q, k, v or out");
+  }
+
   const int bm = attnp::prefill_min_block_m(head_dim);
   const int64_t slots = (T + bm - 1) / bm + cu_q->n_seqs;
-  const int64_t blocks = slots * n_q_heads;
+  const int64_t blocks = slots * n_q_heads * sp.max_pieces;
   if (slots > INT32_MAX || blocks * 1024 >= ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large",
                 (long long)blocks);
@@ -335,6 +475,9 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
     p.score_mult = fabsf(scale) * log2e;
     p.q_mult = scale < 0.f ? -1.f : 1.f;
   }
+  p.piece_tiles = sp.piece_tiles;
+  p.max_pieces = sp.max_pieces;
+  p.partial = sp.piece_tiles > 0 ? static_cast<float*>(workspace) : nullptr;
   const hipError_t e = attnp::launch_prefill(p, head_dim, head_dim_v, (attnp::DType)q->dtype,
                                              (attnp::DType)k->dtype,
                                              reinterpret_cast<hipStream_t>(stream));
@@ -384,15 +527,6 @@ int debug_validate_decode(int64_t n_seqs, const attn_seqlens* cu_k, int64_t Tk,
       return fail(ATTN_ERR_INVALID_ARG, "sequence %lld has %d keys (decode needs >= 1)",
                   (long long)s, lens[s]);
   return ATTN_OK;
-}
-
-// Compute units of the current device (0 if the query fails).
-int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return n;
 }
 
 // Decode work units (sequence, KV head, block of 32 query heads) and the
@@ -619,7 +753,7 @@ int attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
                  int32_t sliding_window, attn_stream_t stream) {
   return run_prefill(q, k, v, out, cu_seqlens, nullptr, nullptr, n_q_heads, n_kv_heads,
-                     head_dim, head_dim, scale, sliding_window, stream);
+                     head_dim, head_dim, scale, sliding_window, nullptr, 0, stream);
 }
 
 int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
@@ -632,7 +766,7 @@ int attn_prefill_chunked(const attn_tensor* q, const attn_tensor* k, const attn_
     return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
   }
   return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, nullptr, n_q_heads, n_kv_heads,
-                     head_dim, head_dim, scale, sliding_window, stream);
+                     head_dim, head_dim, scale, sliding_window, nullptr, 0, stream);
 }
 
 int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
@@ -645,7 +779,7 @@ int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
     return fail(ATTN_ERR_INVALID_ARG, "paged is NULL");
   }
   return run_prefill(q, k_pool, v_pool, out, cu_seqlens_q, nullptr, paged, n_q_heads,
-                     n_kv_heads, head_dim, head_dim, scale, sliding_window, stream);
+                     n_kv_heads, head_dim, head_dim, scale, sliding_window, nullptr, 0, stream);
 }
 
 int attn_prefill_ex(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
@@ -659,7 +793,33 @@ int attn_prefill_ex(const attn_tensor* q, const attn_tensor* k, const attn_tenso
     return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k and paged are both set");
   }
   return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, paged, n_q_heads, n_kv_heads,
-                     head_dim_qk, head_dim_v, scale, sliding_window, stream);
+                     head_dim_qk, head_dim_v, scale, sliding_window, nullptr, 0, stream);
+}
+
+int attn_prefill_ex_ws(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                       const attn_tensor* out, const attn_seqlens* cu_seqlens_q,
+                       const attn_seqlens* cu_seqlens_k, const attn_paged_kv* paged,
+                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim_qk,
+                       int32_t head_dim_v, float scale, int32_t sliding_window, void* workspace,
+                       size_t workspace_bytes, attn_stream_t stream) {
+  if (cu_seqlens_k != nullptr && paged != nullptr) {
+    g_last_error.clear();
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k and paged are both set");
+  }
+  return run_prefill(q, k, v, out, cu_seqlens_q, cu_seqlens_k, paged, n_q_heads, n_kv_heads,
+                     head_dim_qk, head_dim_v, scale, sliding_window, workspace, workspace_bytes,
+                     stream);
+}
+
+size_t attn_prefill_workspace_size(int64_t n_tokens_q, int64_t max_keys, int32_t n_seqs,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim_qk,
+                                   int32_t head_dim_v, int32_t sliding_window) {
+  if (n_tokens_q < 1 || max_keys < 0 || n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 ||
+      n_q_heads % n_kv_heads != 0 || sliding_window < 0)
+    return 0;
+  const SplitPlan sp = plan_prefill_split(n_tokens_q, max_keys, n_seqs, n_q_heads, head_dim_qk,
+                                          head_dim_v, sliding_window);
+  return sp.piece_tiles > 0 ? (size_t)sp.bytes : 0;
 }
 
 const char* attn_prefill_status_string(int status) {

@@ -96,7 +96,31 @@ struct Cfg {
 // ---------------------------------------------------------------- element io
 
 // ------------------------------------------------------------------ kernel
-template <int HDIM, class QT, class KVT, bool PAGED>
+// Key range of one query tile: 64-key tiles [kv_start, kv_start + 64 n) up
+// to the tile's last visible key (kv_hi), from the window start on.
+struct KeyRange {
+  int hist, kv_hi, kv_start, n_tiles;
+};
+__device__ __forceinline__ KeyRange key_range(const PrefillParams& p, const Work& w) {
+  KeyRange r;
+  // Queries are the last len of the sequence's klen positions: local query
+  // i sits at key position hist + i (hist = 0 without a KV history).
+  r.hist = w.klen - w.len;
+  const int q_end = min(w.len, w.q0 + kBM);
+  // the tile's last query sees keys < hist + q_end
+  r.kv_hi = min(max(r.hist + q_end, 0), w.klen);
+  const int kv_lo = p.window > 0 ? min(max(0, r.hist + w.q0 - p.window + 1), r.kv_hi) : 0;
+  r.kv_start = kv_lo - kv_lo % kBN;
+  // at least one (then fully masked) tile keeps the slot schedule uniform
+  // when no key is visible, which only malformed offsets produce
+  r.n_tiles = max(1, (r.kv_hi - r.kv_start + kBN - 1) / kBN);
+  return r;
+}
+
+// SPLIT: the workgroup runs piece (blockIdx / heads) % max_pieces of its
+// query tile's key tiles; a tile of more than one piece leaves fp32
+// partials for prefill_merge_kernel instead of its output.
+template <int HDIM, class QT, class KVT, bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams p) {
   using C = Cfg<HDIM>;
   typedef typename QT::T qelem;
@@ -110,8 +134,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int group = wave >> 2;                                   // 0 = A, 1 = B
-  const int slot = blockIdx.x / p.n_q_heads;
-  const int head = blockIdx.x - slot * p.n_q_heads;
+  const int unit = blockIdx.x / p.n_q_heads;  // slot, or slot * max_pieces + piece
+  const int head = blockIdx.x - unit * p.n_q_heads;
+  const int slot = SPLIT ? unit / p.max_pieces : unit;
+  const int piece = SPLIT ? unit - slot * p.max_pieces : 0;
   Work w = decode_work<kBM, PAGED>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
   w.start = __builtin_amdgcn_readfirstlane(w.start);
@@ -122,17 +148,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   w.klen = __builtin_amdgcn_readfirstlane(w.klen);
 
   const int kvh = head / p.group;
-  // Queries are the last len of the sequence's klen positions: local query
-  // i sits at key position hist + i (hist = 0 without a KV history).
-  const int hist = w.klen - w.len;
-  const int q_end = min(w.len, w.q0 + kBM);
-  // the tile's last query sees keys < hist + q_end
-  const int kv_hi = min(max(hist + q_end, 0), w.klen);
-  const int kv_lo = p.window > 0 ? min(max(0, hist + w.q0 - p.window + 1), kv_hi) : 0;
-  const int kv_start = kv_lo - kv_lo % kBN;
-  // at least one (then fully masked) tile keeps the slot schedule uniform
-  // when no key is visible, which only malformed offsets produce
-  const int n_tiles = max(1, (kv_hi - kv_start + kBN - 1) / kBN);
+  const KeyRange kr = key_range(p, w);
+  const int hist = kr.hist;
+  const int kv_hi = kr.kv_hi;
+  int kv_start = kr.kv_start;
+  int n_tiles = kr.n_tiles;
+  int n_pieces = 1;
+  if (SPLIT) {
+    // at most max_pieces pieces (the grid's and the workspace's bound); the
+    // last one takes every remaining tile
+    n_pieces = min((n_tiles + p.piece_tiles - 1) / p.piece_tiles, p.max_pieces);
+    if (piece >= n_pieces) return;  // uniform: this tile has fewer pieces
+    kv_start += piece * p.piece_tiles * kBN;
+    n_tiles = piece == n_pieces - 1 ? n_tiles - piece * p.piece_tiles : p.piece_tiles;
+  }
 
   const int col = lane & 31;   // query column of this lane
   const int half = lane >> 5;  // which 8-wide half of each 16-wide k-step
@@ -472,10 +501,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     __syncthreads();
   }
 
+  const float l_tot = pair_sum(l_run);
+  if (SPLIT && n_pieces > 1) {
+    // partial of this piece: running max (raw score units), sum, and O
+    // relative to that max, for every row of the tile (rows past the
+    // sequence are written too and never read)
+    float* part = p.partial + (int64_t)blockIdx.x * prefill_partial_floats(HDIM, kBM);
+    const int row = wave * 32 + col;
+    if (half == 0) {
+      part[row] = m_run;
+      part[kBM + row] = l_tot;
+    }
+    // row-major: the lane's four consecutive columns per (block, row group)
+    f32x4_t* po = reinterpret_cast<f32x4_t*>(part + 2 * kBM + row * HDIM);
+#pragma unroll
+    for (int c = 0; c < C::DBLK; ++c)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        po[8 * c + 2 * rb + half] = (f32x4_t){o[c][4 * rb], o[c][4 * rb + 1], o[c][4 * rb + 2],
+                                              o[c][4 * rb + 3]};
+    return;
+  }
+
   // ---- epilogue: O / l -> bf16, rows of this sequence only.  The wave's
   // 32 x HDIM tile goes through its own LDS slice (free after the last
   // barrier) so that every global store writes whole 2*HDIM-byte rows.
-  const float l_tot = pair_sum(l_run);
   if (wave_live) {
     constexpr int OSTR = HDIM + 8;  // row pitch in LDS (bf16 elements)
     static_assert(kWaves * 32 * OSTR <= 2 * C::K_ELEMS + 2 * C::V_ELEMS, "O slices fit");
@@ -511,17 +561,87 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   }
 }
 
+// Combines the pieces of every split query tile: per row,
+// out = sum_i o_i 2^((m_i - M) c) / sum_i l_i 2^((m_i - M) c), M = max_i m_i
+// (the online-softmax combination, across workgroups).  One workgroup per
+// (slot, head, group of kMergeRows rows); thread (row, chunk) handles four
+// consecutive columns of a row, so a wave reads contiguous rows of the
+// partials and writes contiguous bf16 output, and every thread makes one
+// pass (two rounds of independent loads).  Tiles of one piece wrote their
+// output directly.
+template <int HDIM>
+constexpr int merge_rows() { return 256 / (HDIM / 4); }
+
+template <int HDIM, bool PAGED>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
+  constexpr int CH = HDIM / 4;        // 16-byte chunks of a row of partials
+  constexpr int RPP = merge_rows<HDIM>();  // rows per workgroup
+  constexpr int RB = kBM / RPP;       // row groups per query tile
+  constexpr int64_t PF = prefill_partial_floats(HDIM, kBM);
+  const int rb = blockIdx.x % RB;
+  const int sh = blockIdx.x / RB;
+  const int slot = sh / p.n_q_heads;
+  const int head = sh - slot * p.n_q_heads;
+  Work w = decode_work<kBM, PAGED>(p, slot);
+  if (!w.valid) return;
+  const int n_pieces =
+      min((key_range(p, w).n_tiles + p.piece_tiles - 1) / p.piece_tiles, p.max_pieces);
+  if (n_pieces <= 1) return;
+  const float* base =
+      p.partial + ((int64_t)slot * p.max_pieces * p.n_q_heads + head) * PF;
+  const int64_t step = (int64_t)p.n_q_heads * PF;  // next piece of the same tile
+  const int chunk = threadIdx.x % CH;
+  const int row = rb * RPP + threadIdx.x / CH;
+  if (w.q0 + row < w.len) {
+    float mx = -INFINITY;
+    for (int i = 0; i < n_pieces; ++i) mx = fmaxf(mx, base[i * step + row]);
+    float den = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < n_pieces; ++i) {
+      const float* part = base + i * step;
+      const float m = part[row];
+      const float wt = m == -INFINITY ? 0.f : fast_exp2((m - mx) * p.score_mult);
+      den += wt * part[kBM + row];
+      const f32x4_t o = reinterpret_cast<const f32x4_t*>(part + 2 * kBM + row * HDIM)[chunk];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += wt * o[e];
+    }
+    // a row without any visible key (malformed offsets only) is written as zeros
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    u32x2_t v;
+    v[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    v[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) +
+                                (int64_t)(w.start + w.q0 + row) * p.o_ts +
+                                (int64_t)head * p.o_hs + 4 * chunk) = v;
+  }
+}
+
+template <int HDIM, class QT, class KVT, bool PAGED>
+void launch_paged_or_not(const PrefillParams& p, uint64_t slots, hipStream_t stream) {
+  if (p.piece_tiles > 0) {
+    const uint64_t blocks = slots * (uint64_t)p.max_pieces * (uint64_t)p.n_q_heads;
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, true>),
+                       dim3((uint32_t)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((prefill_merge_kernel<HDIM, PAGED>),
+                       dim3((uint32_t)(slots * (uint64_t)p.n_q_heads *
+                                       (uint64_t)(kBM / merge_rows<HDIM>()))),
+                       dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false>),
+                       dim3((uint32_t)(slots * (uint64_t)p.n_q_heads)), dim3(kThreads), 0,
+                       stream, p);
+  }
+}
+
 template <int HDIM, class QT, class KVT>
 hipError_t launch_one(PrefillParams p, hipStream_t stream) {
   const int64_t slots = (p.n_tokens + kBM - 1) / kBM + p.n_seqs;
   p.tile_slots = (int32_t)slots;
-  const uint64_t blocks = (uint64_t)slots * (uint64_t)p.n_q_heads;
   if (p.page_size > 0)
-    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, true>), dim3((uint32_t)blocks),
-                       dim3(kThreads), 0, stream, p);
+    launch_paged_or_not<HDIM, QT, KVT, true>(p, (uint64_t)slots, stream);
   else
-    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, false>), dim3((uint32_t)blocks),
-                       dim3(kThreads), 0, stream, p);
+    launch_paged_or_not<HDIM, QT, KVT, false>(p, (uint64_t)slots, stream);
   return hipGetLastError();
 }
 

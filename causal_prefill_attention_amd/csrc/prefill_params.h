@@ -39,7 +39,22 @@ struct PrefillParams {
   int32_t table_stride;
   int32_t page_size;          // 0 = packed K/V (cu_seqlens_k)
   int32_t n_pages;
+  // Keys split across workgroups (128-d and 64-d kernels, piece_tiles > 0):
+  // the key tiles of each query tile are cut into pieces of piece_tiles
+  // tiles, one workgroup each; a query tile of more than one piece writes
+  // fp32 partial results (running max, sum, unnormalised output) to
+  // `partial` and prefill_merge combines them.
+  int32_t piece_tiles = 0;    // 0 = every query tile in one workgroup
+  int32_t max_pieces = 1;     // grid pieces per query-tile slot
+  float* partial = nullptr;   // [slot][piece][head] blocks of prefill_partial_floats
 };
+
+// fp32 values of one partial block: running max and sum of each of bm rows,
+// then bm x head_dim output values (row-major: value d of row r at
+// 2 * bm + r * head_dim + d).
+constexpr int64_t prefill_partial_floats(int head_dim, int bm) {
+  return (int64_t)bm * (2 + head_dim);
+}
 
 // Smallest number of query rows per workgroup any launch uses (the grid has
 // at most ceil(T / this) + n_seqs tile slots per query head).

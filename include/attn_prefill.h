@@ -194,6 +194,46 @@ int attn_prefill_ex(const attn_tensor* q, const attn_tensor* k,
                     int32_t head_dim_v, float scale, int32_t sliding_window,
                     attn_stream_t stream);
 
+/* attn_prefill_ex with a caller-provided workspace.  When a call has fewer
+ * (query tile, head) pairs than about two per compute unit (a few long
+ * sequences, or few query heads), the 64-key tiles each query tile sees are
+ * cut into pieces of equal length computed by separate workgroups: a query
+ * tile of more than one piece writes per-row running max, softmax sum and
+ * unnormalised output (fp32) to the workspace, and a second kernel on the
+ * same stream rescales the pieces to their common max and writes out, the
+ * online-softmax combination applied across workgroups.  The result equals
+ * attn_prefill_ex up to fp32 rounding order.  Splitting applies to head
+ * sizes (64, 64) and (128, 128); other sizes, calls that already fill the
+ * chip and workspaces smaller than attn_prefill_workspace_size() asks for
+ * run exactly as attn_prefill_ex.
+ *   workspace: device memory, 16-byte aligned, owned by the caller, not
+ *              read before it is written, not overlapping q, k, v or out;
+ *              may be NULL when workspace_bytes == 0
+ * Calls that share a workspace on different streams race.  Other arguments
+ * and errors as for attn_prefill_ex. */
+int attn_prefill_ex_ws(const attn_tensor* q, const attn_tensor* k,
+                       const attn_tensor* v, const attn_tensor* out,
+                       const attn_seqlens* cu_seqlens_q,
+                       const attn_seqlens* cu_seqlens_k,
+                       const attn_paged_kv* paged, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim_qk,
+                       int32_t head_dim_v, float scale, int32_t sliding_window,
+                       void* workspace, size_t workspace_bytes,
+                       attn_stream_t stream);
+
+/* Workspace bytes with which attn_prefill_ex_ws splits a call on the
+ * current device; 0 when it would not split.  n_tokens_q = q->n_tokens;
+ * max_keys bounds any sequence's key count: k->n_tokens for packed or
+ * chunked keys, table_stride * page_size for a paged cache.  For a single
+ * sequence the library compares the finishing time of whole query tiles
+ * with that of pieces (it knows every tile's key count) and splits only for
+ * a clear gain; for several sequences it splits only grids with fewer
+ * workgroups than compute units. */
+size_t attn_prefill_workspace_size(int64_t n_tokens_q, int64_t max_keys,
+                                   int32_t n_seqs, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim_qk,
+                                   int32_t head_dim_v, int32_t sliding_window);
+
 /* Decode: one new query token per sequence (the batched last-token step).
  * Sequence s's query q[s] sits at position Lk - 1 of its Lk keys and sees
  * all of them (with a window W > 0 the last W).  This is

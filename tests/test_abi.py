@@ -497,3 +497,50 @@ def test_ex_empty_batch_is_a_no_op_without_hip():
     for key in ("q", "k", "v", "out"):
         a[key] = mutate(a[key], data=None)
     assert call_ex(a, 320, 256) == B.ATTN_OK
+
+
+# ---- attn_prefill_ex_ws: keys split across workgroups through a workspace
+
+
+def call_ex_ws(a, dqk, dv, workspace, nbytes, seqlens_k=None, paged=None):
+    return B.call_raw_ex_ws(a["q"], a["k"], a["v"], a["out"], a["seqlens"], seqlens_k, paged,
+                            a["n_q_heads"], a["n_kv_heads"], dqk, dv, a["scale"],
+                            a["sliding_window"], workspace, nbytes, None)
+
+
+@pytest.mark.parametrize("name,mut,status,frag", BAD, ids=[b[0] for b in BAD])
+def test_prefill_ws_checks_the_same_arguments(name, mut, status, frag):
+    a = mut(base_args())
+    rc = call_ex_ws(a, a["head_dim"], a["head_dim"], FAKE + (8 << 30), 1 << 20)
+    assert rc == status, (rc, B.last_error())
+    assert frag in B.last_error(), B.last_error()
+
+
+def test_prefill_ws_workspace_checked():
+    a = base_args()
+    rc = call_ex_ws(a, 128, 128, None, 4096)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "workspace is NULL" in B.last_error()
+    rc = call_ex_ws(a, 128, 128, FAKE + (8 << 30) + 4, 4096)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "16-byte aligned" in B.last_error()
+    pg = B.AttnPagedKV(FAKE + (6 << 30), FAKE + (7 << 30), 8, 64)
+    rc = call_ex_ws(a, 128, 128, None, 0, seqlens_k=B.AttnSeqlens(FAKE + (5 << 30), 1, 0),
+                    paged=pg)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "both set" in B.last_error()
+
+
+def test_prefill_ws_unsupported_pairs_rejected_like_ex():
+    a = ex_args()
+    assert call_ex_ws(a, 320, 128, None, 0) == B.ATTN_ERR_UNSUPPORTED
+    assert "head_dim 320 / head_dim_v 128" in B.last_error()
+
+
+@pytest.mark.parametrize("args", [(0, 100, 1, 4, 1, 128, 128, 0),
+                                  (100, 100, 0, 4, 1, 128, 128, 0),
+                                  (100, 100, 1, 6, 4, 128, 128, 0),
+                                  (100, -1, 1, 4, 1, 128, 128, 0),
+                                  (100, 100, 1, 4, 1, 128, 128, -1),
+                                  (8192, 8192, 1, 4, 1, 320, 256, 0),
+                                  (8192, 8192, 1, 4, 1, 256, 256, 0)])
+def test_prefill_workspace_size_is_zero_outside_the_split(args):
+    # bad shapes, and head sizes without a split (also zero with no GPU)
+    assert B.prefill_workspace_size(*args) == 0

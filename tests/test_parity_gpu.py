@@ -320,6 +320,106 @@ def test_full_size_sampled(name):
     assert np.all(np.isfinite(got)), "non-finite output somewhere"
 
 
+# ------------------------------------- prefill keys split across workgroups
+def run_ws(inp, hq, hkv, d, scale, window, workspace, paged=None):
+    dev = torch.device("cuda:0")
+    q = inp["q"].to(dev)
+    out = torch.empty(q.shape[0], hq, d, dtype=torch.bfloat16, device=dev)
+    if paged is None:
+        k, v = inp["k"].to(dev), inp["v"].to(dev)
+        cuk = inp["cu_seqlens_k"].to(dev) if "cu_seqlens_k" in inp else None
+        pg = None
+    else:
+        k_pool, v_pool, table, page = paged
+        k, v = k_pool.to(dev), v_pool.to(dev)
+        cuk = None
+        pg = (torch.from_numpy(table).to(dev),
+              torch.tensor(inp["kv_lengths"], dtype=torch.int32, device=dev), page)
+    binding.attn_prefill_ex(q, k, v, out, inp["cu_seqlens"].to(dev), hq, hkv, d, d, scale,
+                            window, cu_seqlens_k=cuk, paged=pg, workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def split_workspace(inp, hq, hkv, d, max_keys=None, windows=(0,)):
+    """A workspace for every listed window (the plan, and so its size,
+    depends on the window), filled with NaN bytes: nothing may read a
+    partial before it is written."""
+    T = inp["q"].shape[0]
+    n_seqs = len(inp["lengths"])
+    mk = max_keys if max_keys is not None else inp["k"].shape[0]
+    sizes = [binding.prefill_workspace_size(T, mk, n_seqs, hq, hkv, d, d, win)
+             for win in windows]
+    assert min(sizes) > 0, f"this shape is split at every window: {sizes}"
+    nbytes = max(sizes)
+    # NaN bytes: nothing may read a partial before it is written
+    return torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_split_packed(d):
+    """A long and a short sequence (query tiles of one and of several
+    pieces in one launch), 2 query heads on 1 KV head: against the oracle and
+    against the unsplit kernel, causal, with windows and scale signs."""
+    w = workloads.custom(f"split_d{d}", [3000, 200, 1], 2, 1, head_dim=d, seed=151,
+                         k_outlier_frac=0.01)
+    inp = workloads.make_inputs(w)
+    ws = split_workspace(inp, 2, 1, d, windows=(0, 1, 700))
+    for win in (0, 1, 700):
+        for scale in (1 / math.sqrt(d), -0.5):
+            _announce(f"{w.name} W={win} s={scale:.3f}")
+            out = run_ws(inp, 2, 1, d, scale, win, ws)
+            check(f"split_d{d}_w{win}_s{scale:.3f}", to64(out), oracle_of(inp, 2, 1, scale, win))
+            ref = run_gpu(inp, 2, 1, d, scale, win)
+            diff = float((out.float() - ref.float()).abs().max())
+            assert diff <= 2e-2, f"split vs unsplit: {diff}"
+
+
+def test_prefill_split_chunked_paged_and_dtypes():
+    w = workloads.custom("split_chunked", [900, 64], 4, 2, seed=152, q_dtype="fp32",
+                         kv_dtype="fp16", history=[2500, 10])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    ws = split_workspace(inp, 4, 2, 128, windows=(0, 500))
+    for win in (0, 500):
+        out = run_ws(inp, 4, 2, 128, w.attn_scale, win, ws)
+        check(f"split_chunked_w{win}", to64(out), oracle_of(inp, 4, 2, w.attn_scale, win))
+    k_pool, v_pool, table = to_paged(inp, 128, seed=15)
+    wsp = split_workspace(inp, 4, 2, 128, max_keys=table.shape[1] * 128)
+    out = run_ws(inp, 4, 2, 128, w.attn_scale, 0, wsp, paged=(k_pool, v_pool, table, 128))
+    want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                  inp["kv_lengths"], 128, 4, 2, w.attn_scale, 0)
+    check("split_paged", to64(out), want)
+
+
+def test_prefill_split_small_workspace_is_the_unsplit_kernel():
+    """A workspace smaller than the split needs runs the unsplit kernel:
+    the same bits as attn_prefill."""
+    w = workloads.custom("split_small_ws", [2000], 2, 1, seed=153)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    full = split_workspace(inp, 2, 1, 128)
+    small = torch.empty(full.numel() // 2, dtype=torch.uint8, device="cuda:0")
+    out = run_ws(inp, 2, 1, 128, w.attn_scale, 0, small)
+    assert torch.equal(out, run_gpu(inp, 2, 1, 128, w.attn_scale, 0))
+
+
+@pytest.mark.parametrize("name", ["long_8192tok_4q1kv_outliers_share"])
+def test_prefill_split_full_size_sampled(name):
+    """The benchmark workloads that split, with the workspace the benchmark
+    passes, on sampled rows."""
+    w = workloads.WORKLOADS[name]
+    _announce(f"{name} split")
+    inp = workloads.make_inputs(w)
+    ws = split_workspace(inp, w.n_q_heads, w.n_kv_heads, w.head_dim, windows=(w.window,))
+    out = to64(run_ws(inp, w.n_q_heads, w.n_kv_heads, w.head_dim, w.attn_scale, w.window, ws))
+    rows = workloads.sample_rows(inp["lengths"], w.n_q_heads, 256, seed=w.seed)
+    want = oracle.attention_rows(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                 w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window, rows)
+    check(f"{name}_split_sampled", np.stack([out[t, h] for t, h in rows]), want)
+    assert np.all(np.isfinite(out))
+
+
 # ------------------------------------------------------------ size limits
 def test_many_short_sequences_every_kernel():
     """300 sequences (the work decode scans the offsets 64 at a time, so this
