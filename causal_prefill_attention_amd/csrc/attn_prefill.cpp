@@ -244,8 +244,9 @@ double list_makespan(const std::vector<double>& jobs, int64_t cus) {
   return end;
 }
 
-SplitPlan plan_prefill_split(int64_t T, int64_t max_keys, int64_t n_seqs, int32_t n_q_heads,
-                             int32_t head_dim, int32_t head_dim_v, int32_t window) {
+SplitPlan plan_prefill_split_uncached(int64_t T, int64_t max_keys, int64_t n_seqs,
+                                      int32_t n_q_heads, int32_t head_dim, int32_t head_dim_v,
+                                      int32_t window) {
   SplitPlan sp;
   if (head_dim != head_dim_v || (head_dim != 128 && head_dim != 64) || T <= 0) return sp;
   const int64_t bm = attnp::prefill_min_block_m(head_dim);
@@ -322,6 +323,32 @@ SplitPlan plan_prefill_split(int64_t T, int64_t max_keys, int64_t n_seqs, int32_
   const int64_t pieces = (max_nt + c - 1) / c;
   if (pieces < 2 || c > INT32_MAX) return sp;
   return finish((int32_t)c, pieces);
+}
+
+// The plan of the last call on this thread is kept: a serving loop repeats
+// the same shapes, and one plan costs up to ~0.1 ms of host time.
+SplitPlan plan_prefill_split(int64_t T, int64_t max_keys, int64_t n_seqs, int32_t n_q_heads,
+                             int32_t head_dim, int32_t head_dim_v, int32_t window) {
+  struct Key {
+    int64_t T, max_keys, n_seqs;
+    int32_t n_q_heads, head_dim, head_dim_v, window;
+    int dev;
+    bool operator==(const Key& o) const {
+      return T == o.T && max_keys == o.max_keys && n_seqs == o.n_seqs &&
+             n_q_heads == o.n_q_heads && head_dim == o.head_dim && head_dim_v == o.head_dim_v &&
+             window == o.window && dev == o.dev;
+    }
+  };
+  thread_local Key last_key{-1, -1, -1, 0, 0, 0, 0, -1};
+  thread_local SplitPlan last_plan;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  const Key key{T, max_keys, n_seqs, n_q_heads, head_dim, head_dim_v, window, dev};
+  if (key == last_key) return last_plan;
+  last_plan =
+      plan_prefill_split_uncached(T, max_keys, n_seqs, n_q_heads, head_dim, head_dim_v, window);
+  last_key = key;
+  return last_plan;
 }
 
 int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,

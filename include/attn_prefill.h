@@ -228,7 +228,10 @@ int attn_prefill_ex_ws(const attn_tensor* q, const attn_tensor* k,
  * sequence the library compares the finishing time of whole query tiles
  * with that of pieces (it knows every tile's key count) and splits only for
  * a clear gain; for several sequences it splits only grids with fewer
- * workgroups than compute units. */
+ * workgroups than compute units.  Planning a single sequence takes up to a
+ * few hundred microseconds of host time; the plan of the last shape is kept
+ * per thread, so repeated calls cost about a microsecond.  Call it once the
+ * device is initialised (it reads the device's compute-unit count). */
 size_t attn_prefill_workspace_size(int64_t n_tokens_q, int64_t max_keys,
                                    int32_t n_seqs, int32_t n_q_heads,
                                    int32_t n_kv_heads, int32_t head_dim_qk,
