@@ -9,24 +9,28 @@
 //
 // Design (ours, for CDNA4): a 512-d head would need 256 fp32 accumulator
 // and 128 Q operand registers in one 32-row wave, beyond one wave's
-// budget.  Instead the four waves of a workgroup (one per SIMD) share the
-// same 32 query rows and split the head dimension: wave w owns columns
-// [128w, 128w + 128) of Q, K, V and out.
-//   * Per 64-key tile, wave w forms the partial scores Sᵀ_w = K_w Q_wᵀ from
-//     its 128 columns (16 MFMAs, 32x32x16 bf16), the four partials are
-//     summed through LDS in a fixed order (so every wave holds the same fp32
-//     scores), every wave runs the same online softmax (the same P, running
-//     max and sum in all four), and wave w accumulates Oᵀ_w += Vᵀ_w Pᵀ for
-//     its 128 output columns (16 MFMAs).  No MFMA work is repeated.
-//   * A wave only ever reads its own columns of K and V, so it stages them
-//     privately: coalesced 16-byte loads one tile ahead into registers, bf16
-//     conversion, a store into its own LDS slice with 16-byte chunks of row
-//     r at position (chunk ^ (r & 15)); K operands are read row-wise, Vᵀ
-//     operands with ds_read_b64_tr_b16 (four keys of one column per lane, in
-//     the Sᵀ accumulator's key order).
-//   * Two barriers per tile fence the 32 KiB score exchange (16-byte LDS
-//     writes and reads); LDS holds four 32 KiB K/V slices plus the
-//     exchange, 160 KiB in all.
+// budget.  The head is split by columns instead, and the split is laid over
+// the 128-d kernel's ping-pong:
+//   * Eight waves in two groups, A (waves 0-3) and B (4-7), each group one
+//     32-row query block (64 rows per workgroup).  Wave w of a group owns
+//     columns [128w, 128w + 128) of Q, K, V and out, so waves w and w + 4 --
+//     one SIMD -- share that column slice of every K/V tile.
+//   * Per 32-key tile a wave forms partial scores Sᵀ_w = K_w Q_wᵀ from its
+//     columns (8 MFMAs, 32x32x16 bf16) and writes them to its group's LDS
+//     exchange; in the group's next slot every wave sums the four partials
+//     in the same order (so all four hold the same fp32 scores), runs the
+//     same online softmax, and later accumulates Oᵀ_w += Vᵀ_w Pᵀ for its 128
+//     output columns (8 MFMAs).  No MFMA work is repeated.
+//   * The groups run in anti-phase as in the 128-d kernel: in one slot group
+//     A issues its MFMAs (P.V of the previous tile, then the partial scores
+//     of this one) while group B runs its exchange and softmax, and the
+//     next slot the other way round, so the matrix core of each SIMD is fed
+//     by one wave while the vector ALU works for the other.
+//   * Group A stages the K column slices and group B the V slices through
+//     registers into two LDS stages (rows of 128 bf16, 16-byte chunks of row
+//     r at position chunk ^ (r & 15)); Vᵀ operands come from the transposing
+//     LDS read ds_read_b64_tr_b16.  LDS: 128 KiB of K/V stages and 32 KiB of
+//     exchange.
 #include <hip/hip_runtime.h>
 #include <climits>
 #include <stdint.h>
@@ -43,33 +47,35 @@ using namespace dev;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGWave = 64;
-constexpr int kGWaves = 4;                  // one per SIMD, one column slice each
+constexpr int kGWaves = 8;                  // two groups of four
 constexpr int kGThreads = kGWave * kGWaves;
-constexpr int kGHead = 512;                 // head size of q, k, v and out
-constexpr int kGSlice = kGHead / kGWaves;   // 128 columns per wave
-constexpr int kGBM = 32;                    // query rows per workgroup
-constexpr int kGBN = 64;                    // keys per tile
+constexpr int kGSlices = 4;                 // column slices (one wave per group each)
+constexpr int kGSlice = 512 / kGSlices;     // 128 columns per slice
+constexpr int kGBM = 64;                    // query rows per workgroup (32 per group)
+constexpr int kGBN = 32;                    // keys per tile: one 32-key score block
+constexpr int kGKQ = kGBN / 16;             // 16-key P.V steps per tile
 constexpr float kGLazy = 8.0f;              // lazy-max threshold, log2 units
 
 template <class QT, class KVT, bool PAGED>
 __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParams p) {
-  constexpr int CPR = kGSlice / 8;          // 16-byte chunks per slice row
-  constexpr int DCH = kGSlice / 16;         // score k-steps per wave
-  constexpr int DBLK = kGSlice / 32;        // output blocks per wave
-  constexpr int TILE = kGBN * kGSlice;      // elements of one K (or V) slice tile
+  constexpr int CPR = kGSlice / 8;            // 16-byte chunks per slice row
+  constexpr int DCH = kGSlice / 16;           // score k-steps per slice
+  constexpr int DBLK = kGSlice / 32;          // output blocks per slice
+  constexpr int TILE = kGBN * kGSlice;        // elements of one K or V slice tile
   constexpr int LOADS = kGBN * CPR / kGWave;  // 16-byte chunks per lane per tile
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
 
-  // per wave: K slice tile then V slice tile (bf16, rows of 128, swizzled)
-  __shared__ __attribute__((aligned(16))) uint16_t kvs[kGWaves * 2 * TILE];
-  // partial scores of every wave: [wave][kb][r / 4][lane] x 4 floats
-  __shared__ __attribute__((aligned(16))) f32x4_t xch[kGWaves * 2 * 4 * kGWave];
+  // [stage][slice][K, V][TILE] bf16, then the exchange [group][slice][r/4][lane]
+  __shared__ __attribute__((aligned(16))) uint16_t kvs[2 * kGSlices * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) f32x4_t xch[2 * kGSlices * 4 * kGWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kGWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kGWave);
-  const int col = lane & 31;   // query column of this lane
+  const int group = wave >> 2;  // 0 = A (stages K), 1 = B (stages V)
+  const int sl = wave & 3;      // column slice
+  const int col = lane & 31;    // query column of this lane
   const int half = lane >> 5;
   const int slot = blockIdx.x / p.n_q_heads;
   const int head = blockIdx.x - slot * p.n_q_heads;
@@ -89,18 +95,19 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   const int kv_lo = p.window > 0 ? min(max(0, hist + w.q0 - p.window + 1), kv_hi) : 0;
   const int kv_start = kv_lo - kv_lo % kGBN;
   const int n_tiles = max(1, (kv_hi - kv_start + kGBN - 1) / kGBN);
-  const int q_last = min(w.q0 + kGBM - 1, w.len - 1);
-  const int myq = w.q0 + col;
+  const int wq0 = w.q0 + 32 * group;  // this group's query block
+  const int wq_last = min(wq0 + 31, w.len - 1);
+  const int myq = wq0 + col;
   const int mypos = hist + myq;
-  const int d0 = wave * kGSlice;  // first column of this wave's slice
+  const int d0 = sl * kGSlice;  // first column of this wave's slice
 
-  // ---- K/V slice tiles: lane moves chunk (lane % CPR) of rows 4i + lane / CPR
-  const kvelem* kbase = static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts +
-                        (int64_t)kvh * p.k_hs + d0;
-  const kvelem* vbase = static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts +
-                        (int64_t)kvh * p.v_hs + d0;
-  const int k_row_bytes = (int)(p.k_ts * (int64_t)sizeof(kvelem));
-  const int v_row_bytes = (int)(p.v_ts * (int64_t)sizeof(kvelem));
+  // ---- K (group A) or V (group B) slice tiles: lane moves chunk
+  // (lane % CPR) of rows 4i + lane / CPR
+  const kvelem* src = group == 0
+      ? static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts + (int64_t)kvh * p.k_hs + d0
+      : static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts + (int64_t)kvh * p.v_hs + d0;
+  const int64_t src_ts = group == 0 ? p.k_ts : p.v_ts;
+  const int row_bytes = (int)(src_ts * (int64_t)sizeof(kvelem));
   auto tile_slot = [&](int kv0) -> int64_t {
     if (!PAGED) return kv0;
     const int* row = p.block_table + (int64_t)w.seq * p.table_stride;
@@ -108,169 +115,81 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
     const int page = min(max(row[idx], 0), p.n_pages - 1);
     return (int64_t)page * p.page_size + (kv0 - idx * p.page_size);
   };
-  u32x4_t kr[LOADS], vr[LOADS];
+  u32x4_t st_regs[LOADS];
   auto gload = [&](int kv0) {
     // rows past the last visible key read as zero (buffer range)
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kv_hi - kv0, kGBN)));
-    const int64_t ts = tile_slot(kv0);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<kvelem*>(kbase + ts * p.k_ts), 0, rows * k_row_bytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<kvelem*>(vbase + ts * p.v_ts), 0, rows * v_row_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<kvelem*>(src + tile_slot(kv0) * src_ts), 0, rows * row_bytes, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int row = i * (kGWave / CPR) + lane / CPR;
-      const int ch = lane % CPR;
-      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, row * k_row_bytes + 16 * ch, 0, 0);
-      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, row * v_row_bytes + 16 * ch, 0, 0);
+      st_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(r, row * row_bytes + 16 * (lane % CPR),
+                                                         0, 0);
     }
   };
-  uint16_t* const kt = kvs + wave * 2 * TILE;
-  uint16_t* const vt = kt + TILE;
-  auto lstore = [&]() {
+  auto kslice = [&](int st) { return kvs + ((st * kGSlices + sl) * 2 + 0) * TILE; };
+  auto vslice = [&](int st) { return kvs + ((st * kGSlices + sl) * 2 + 1) * TILE; };
+  auto lstore = [&](int st) {  // group A: K stage st; group B: V stage st
+    uint16_t* dst = group == 0 ? kslice(st) : vslice(st);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int row = i * (kGWave / CPR) + lane / CPR;
       const int pos = (lane % CPR) ^ (row & 15);
-      *reinterpret_cast<u32x4_t*>(kt + row * kGSlice + 8 * pos) = kv_to_bf16(KVT(), kr[i]);
-      *reinterpret_cast<u32x4_t*>(vt + row * kGSlice + 8 * pos) = kv_to_bf16(KVT(), vr[i]);
+      *reinterpret_cast<u32x4_t*>(dst + row * kGSlice + 8 * pos) = kv_to_bf16(KVT(), st_regs[i]);
     }
   };
 
-  // first tile in flight before Q, so that the two latencies overlap
-  gload(kv_start);
-
   // ---- Qᵀ operand of this wave's slice: lane holds q[myq, d0 + 16c + 8*half ..]
   bf16x8_t qf[DCH];
-  {
-    const qelem* qrow = static_cast<const qelem*>(p.q) +
-                        (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
-                        (int64_t)head * p.q_hs + d0;
-    load_q_operand<DCH>(qrow, half, myq < w.len ? p.q_mult : 0.f, qf);
-  }
+  const qelem* const qrow = static_cast<const qelem*>(p.q) +
+                            (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
+                            (int64_t)head * p.q_hs + d0;
+  const float qmul = myq < w.len ? p.q_mult : 0.f;
 
-  // ---- per-wave state (m_run and l_run are the same in all four waves)
+  // ---- per-wave state (the four waves of a group keep the same m and l)
   f32x16_t o[DBLK];
 #pragma unroll
   for (int c = 0; c < DBLK; ++c) o[c] = (f32x16_t){};
+  bf16x8_t pf[kGKQ];
   float m_run = -INFINITY;
   float l_run = 0.f;
   const float cmul = p.score_mult;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-  f32x4_t* const xw = xch + wave * 2 * 4 * kGWave;
+  f32x4_t* const xg = xch + group * kGSlices * 4 * kGWave;  // this group's exchange
+  f32x4_t* const xw = xg + sl * 4 * kGWave;                   // this wave's partial
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = kv_start + t * kGBN;
-    lstore();  // tile t: registers -> this wave's slice (read by this wave only)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (t + 1 < n_tiles) gload(kv0 + kGBN);  // tile t+1 in flight meanwhile
-
-    // partial Sᵀ = K_w Q_wᵀ: keys on M (two 32-key blocks), queries on N
-    f32x16_t sc[2];
+  // partial Sᵀ = K_w Q_wᵀ of the tile in K stage st, to the exchange
+  auto scores = [&](int st) {
+    const uint16_t* kt = kslice(st);
+    f32x16_t sc = (f32x16_t){};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = (f32x16_t){};
-      const int row = 32 * kb + col;
-#pragma unroll
-      for (int c = 0; c < DCH; ++c) {
-        const int pos = (2 * c + half) ^ (row & 15);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + row * kGSlice + 8 * pos);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[kb], 0, 0, 0);
-      }
+    for (int c = 0; c < DCH; ++c) {
+      const int pos = (2 * c + half) ^ (col & 15);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + col * kGSlice + 8 * pos);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc, 0, 0, 0);
     }
-    // exchange: every wave finished reading the previous tile's partials
-    __syncthreads();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        xw[(kb * 4 + r4) * kGWave + lane] = (f32x4_t){sc[kb][4 * r4], sc[kb][4 * r4 + 1],
-                                                      sc[kb][4 * r4 + 2], sc[kb][4 * r4 + 3]};
-    __syncthreads();
-    // full scores, summed in wave order 0..3 in every wave
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4_t acc = xch[(kb * 4 + r4) * kGWave + lane];
-#pragma unroll
-        for (int v = 1; v < kGWaves; ++v) acc += xch[((v * 2 + kb) * 4 + r4) * kGWave + lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[kb][4 * r4 + e] = acc[e];
-      }
-
-    // mask the causal diagonal, the window start and the key count
-    const bool full = (kv0 + kGBN - 1 <= hist + w.q0) &&
-                      (p.window == 0 || kv0 >= hist + q_last - p.window + 1);
-    if (!full) {
-      // key = kv0 + 4*half + off, off = 32*kb + 8*(r/4) + r%4 (compile-time):
-      // visible when off <= hi and, with a window, off >= lo
-      const int hi = mypos - kv0 - 4 * half;
-      // (lo <= 0 bounds nothing since off >= 0: the subtraction only runs where it
-      // cannot overflow; no branch, the same code with and without a window)
-      const int lo = (p.window > 0 && p.window <= hi) ? hi - p.window + 1 : INT_MIN;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-          if (off > hi || off < lo) sc[kb][r] = -INFINITY;
-        }
-    }
-    // online softmax (lazy max, base 2) into the bf16 Pᵀ operand
-    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], sc[kb][r]);
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = pair_max(mx);
-    const bool raise = (mx - m_run) * cmul > kGLazy;
-    const bool any = __ballot(raise) != 0ull;
-    const float m_new = any ? fmaxf(m_run, mx) : m_run;
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
-    const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
-    m_run = m_new;
-    bf16x8_t pf[4];
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
-      u32x4_t u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(sc[kq >> 1][8 * (kq & 1) + 2 * e], cmul, neg_mc));
-        const float p1 = fast_exp2(fmaf(sc[kq >> 1][8 * (kq & 1) + 2 * e + 1], cmul, neg_mc));
-        // (the converted pair feeds the dot product directly; see the 128-d kernel)
-        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
-        u[e] = __builtin_bit_cast(uint32_t, pb);
-        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
-      }
-      pf[kq] = __builtin_bit_cast(bf16x8_t, u);
-    }
-    l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
-    if (any) {
-#pragma unroll
-      for (int c = 0; c < DBLK; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-    }
-
-    // Oᵀ_w += Vᵀ_w Pᵀ.  MFMA k-index 8*half + e of step kq is key
-    // 16*kq + 8*(e / 4) + 4*half + e % 4 (the Sᵀ accumulator's order): two
-    // transposing reads give keys +0..3 and +8..11 (+4*half) of column d.
-    const int grp = (lane >> 4) & 1;  // 16-column half of the 32-row block
+    for (int r4 = 0; r4 < 4; ++r4)
+      xw[r4 * kGWave + lane] = (f32x4_t){sc[4 * r4], sc[4 * r4 + 1], sc[4 * r4 + 2],
+                                         sc[4 * r4 + 3]};
+  };
+  // Oᵀ_w += Vᵀ_w Pᵀ for the tile in V stage st.  MFMA k-index 8*half + e of
+  // step kq is key 16*kq + 8*(e / 4) + 4*half + e % 4 (the Sᵀ accumulator's
+  // order): two transposing reads give keys +0..3 and +8..11 (+4*half).
+  auto pv = [&](int st) {
+    const uint16_t* vt = vslice(st);
+    const int grp16 = (lane >> 4) & 1;  // 16-column half of the 32-row block
     const int j = lane & 15;
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
+    for (int kq = 0; kq < kGKQ; ++kq) {
 #pragma unroll
       for (int c = 0; c < DBLK; ++c) {
         s16x4_t part[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int row = 16 * kq + 8 * r + 4 * half + (j >> 2);
-          const int d = 32 * c + 16 * grp + 4 * (j & 3);
+          const int d = 32 * c + 16 * grp16 + 4 * (j & 3);
           const int pos = (d >> 3) ^ (row & 15);
           part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4_t*)(vt + row * kGSlice + 8 * pos +
@@ -285,8 +204,131 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
                                                        o[c], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+  };
+  // the group's four partials summed in slice order, masks, online softmax
+  auto softmax = [&](int kv0) {
+    f32x16_t sc;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4_t acc = xg[r4 * kGWave + lane];
+#pragma unroll
+      for (int v = 1; v < kGSlices; ++v) acc += xg[(v * 4 + r4) * kGWave + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[4 * r4 + e] = acc[e];
+    }
+    const bool full = (kv0 + kGBN - 1 <= hist + wq0) &&
+                      (p.window == 0 || kv0 >= hist + wq_last - p.window + 1);
+    if (!full) {
+      // key = kv0 + 4*half + off, off = 8*(r/4) + r%4 (compile-time): visible
+      // when off <= hi and, with a window, off >= lo (lo <= 0 bounds nothing
+      // since off >= 0; the subtraction only runs where it cannot overflow)
+      const int hi = mypos - kv0 - 4 * half;
+      const int lo = (p.window > 0 && p.window <= hi) ? hi - p.window + 1 : INT_MIN;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        if (off > hi || off < lo) sc[r] = -INFINITY;
+      }
+    }
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], sc[r]);
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    mx = pair_max(mx);
+    const bool raise = (mx - m_run) * cmul > kGLazy;
+    const bool any = __ballot(raise) != 0ull;
+    const float m_new = any ? fmaxf(m_run, mx) : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
+    const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
+    m_run = m_new;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < kGKQ; ++kq) {
+      u32x4_t u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(sc[8 * kq + 2 * e], cmul, neg_mc));
+        const float p1 = fast_exp2(fmaf(sc[8 * kq + 2 * e + 1], cmul, neg_mc));
+        // (the converted pair feeds the dot product directly; see the 128-d kernel)
+        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        u[e] = __builtin_bit_cast(uint32_t, pb);
+        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
+      }
+      pf[kq] = __builtin_bit_cast(bf16x8_t, u);
+    }
+    l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
+    if (any) {
+#pragma unroll
+      for (int c = 0; c < DBLK; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
+    }
+  };
+
+  // ---- prologue: K(0) stored (group A), V(0) in flight (group B), Q loaded
+  // once the first tile's loads are issued
+  gload(kv_start);
+  load_q_operand<DCH>(qrow, half, qmul, qf);
+  if (group == 0) {
+    lstore(0);
+    if (n_tiles > 1) gload(kv_start + kGBN);
+  }
+  __syncthreads();
+
+  // ---- ping-pong slots (the 128-d kernel's schedule).  In slot 2j group A
+  // runs its matrix work for tile j (P(j-1)V(j-1), then partial S(j) to its
+  // exchange) while group B runs softmax(j-1) from its exchange; in slot
+  // 2j+1 the other way round.  K(j) (stage j&1) is read in slots 2j and
+  // 2j+1, V(j) (stage j&1) in slots 2j+2 and 2j+3.  Group A writes K(j+1)
+  // in its softmax slot 2j+1, group B writes V(j) after its matrix work in
+  // slot 2j+1; each load has two slots to arrive.  A group's exchange is
+  // written in its matrix slot and read in its next slot, after the
+  // barrier.  Both groups pass the same 2n + 2 barriers after the prologue.
+  if (group == 0) {
+    scores(0);
+    __syncthreads();
+    softmax(kv_start);
+    if (n_tiles > 1) {
+      lstore(1);
+      if (n_tiles > 2) gload(kv_start + 2 * kGBN);
+    }
+    __syncthreads();
+    for (int j = 1; j < n_tiles; ++j) {
+      const int kv0 = kv_start + j * kGBN;
+      pv((j - 1) & 1);
+      scores(j & 1);
+      __syncthreads();
+      softmax(kv0);
+      if (j + 1 < n_tiles) {
+        lstore((j + 1) & 1);
+        if (j + 2 < n_tiles) gload(kv0 + 2 * kGBN);
+      }
+      __syncthreads();
+    }
+    pv((n_tiles - 1) & 1);
+    __syncthreads();
+    __syncthreads();
+  } else {
+    __syncthreads();
+    // V(0) was loaded before the first barrier
+    scores(0);
+    lstore(0);
+    if (n_tiles > 1) gload(kv_start + kGBN);
+    __syncthreads();
+    softmax(kv_start);
+    __syncthreads();
+    for (int j = 1; j < n_tiles; ++j) {
+      const int kv0 = kv_start + j * kGBN;
+      pv((j - 1) & 1);
+      scores(j & 1);
+      lstore(j & 1);
+      if (j + 1 < n_tiles) gload(kv0 + kGBN);
+      __syncthreads();
+      softmax(kv0);
+      __syncthreads();
+    }
+    pv((n_tiles - 1) & 1);
+    __syncthreads();
   }
 
   // ---- epilogue: O_w / l -> bf16, 4 consecutive columns per lane and block
