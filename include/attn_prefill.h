@@ -181,8 +181,9 @@ int attn_prefill_paged(const attn_tensor* q, const attn_tensor* k_pool,
  * with the key layout of attn_prefill (cu_seqlens_k and paged both NULL),
  * attn_prefill_chunked (cu_seqlens_k set) or attn_prefill_paged (paged
  * set; both set is ATTN_ERR_INVALID_ARG).  Supported pairs: (64, 64),
- * (128, 128), (256, 256) and (320, 256), the absorbed MLA prefill of atlas
- * PR #69 (q = [q_absorbed | q_rope] against the compressed cache row
+ * (128, 128), (256, 256), (512, 512) and (320, 256), the absorbed MLA
+ * prefill of atlas PR #69 (q = [q_absorbed | q_rope] against the
+ * compressed cache row
  * [kv_latent | k_rope], v = the kv_latent part of the same row -- a view of
  * k with the same token stride -- and scale 1/sqrt(320)); others are
  * ATTN_ERR_UNSUPPORTED. */
