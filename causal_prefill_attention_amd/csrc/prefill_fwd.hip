@@ -101,12 +101,13 @@ struct Cfg {
 struct KeyRange {
   int hist, kv_hi, kv_start, n_tiles;
 };
+template <int BM>
 __device__ __forceinline__ KeyRange key_range(const PrefillParams& p, const Work& w) {
   KeyRange r;
   // Queries are the last len of the sequence's klen positions: local query
   // i sits at key position hist + i (hist = 0 without a KV history).
   r.hist = w.klen - w.len;
-  const int q_end = min(w.len, w.q0 + kBM);
+  const int q_end = min(w.len, w.q0 + BM);
   // the tile's last query sees keys < hist + q_end
   r.kv_hi = min(max(r.hist + q_end, 0), w.klen);
   const int kv_lo = p.window > 0 ? min(max(0, r.hist + w.q0 - p.window + 1), r.kv_hi) : 0;
@@ -120,8 +121,15 @@ __device__ __forceinline__ KeyRange key_range(const PrefillParams& p, const Work
 // SPLIT: the workgroup runs piece (blockIdx / heads) % max_pieces of its
 // query tile's key tiles; a tile of more than one piece leaves fp32
 // partials for prefill_merge_kernel instead of its output.
-template <int HDIM, class QT, class KVT, bool PAGED, bool SPLIT>
+// HP: query heads per workgroup.  With HP = 4 (the heads of one group of
+// four sharing a KV head) the workgroup covers 64 rows of each of the four
+// heads: wave w runs head 4 * group_index + w % 4 on rows 32 * (w / 4) ..
+// +31 of the tile, so every K/V tile staged in LDS serves four heads and a
+// query tile's causal diagonal spans one key tile instead of four.
+template <int HDIM, class QT, class KVT, bool PAGED, bool SPLIT, int HP>
 __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams p) {
+  static_assert(HP == 1 || (HP == 4 && !SPLIT), "head packing is for unsplit tiles");
+  constexpr int BMQ = kBM / HP;  // query rows per head
   using C = Cfg<HDIM>;
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
@@ -134,11 +142,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int group = wave >> 2;                                   // 0 = A, 1 = B
-  const int unit = blockIdx.x / p.n_q_heads;  // slot, or slot * max_pieces + piece
-  const int head = blockIdx.x - unit * p.n_q_heads;
+  const int n_units = p.n_q_heads / HP;       // workgroups per tile slot (and piece)
+  const int unit = blockIdx.x / n_units;      // slot, or slot * max_pieces + piece
+  const int hbase = (blockIdx.x - unit * n_units) * HP;
+  const int head = hbase + (HP == 1 ? 0 : (wave & (HP - 1)));  // wave-uniform
   const int slot = SPLIT ? unit / p.max_pieces : unit;
   const int piece = SPLIT ? unit - slot * p.max_pieces : 0;
-  Work w = decode_work<kBM, PAGED>(p, slot);
+  Work w = decode_work<BMQ, PAGED>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
   w.start = __builtin_amdgcn_readfirstlane(w.start);
   w.len = __builtin_amdgcn_readfirstlane(w.len);
@@ -147,8 +157,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   w.seq = __builtin_amdgcn_readfirstlane(w.seq);
   w.klen = __builtin_amdgcn_readfirstlane(w.klen);
 
-  const int kvh = head / p.group;
-  const KeyRange kr = key_range(p, w);
+  const int kvh = hbase / p.group;  // the same for every head of the workgroup
+  const KeyRange kr = key_range<BMQ>(p, w);
   const int hist = kr.hist;
   const int kv_hi = kr.kv_hi;
   int kv_start = kr.kv_start;
@@ -165,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 
   const int col = lane & 31;   // query column of this lane
   const int half = lane >> 5;  // which 8-wide half of each 16-wide k-step
-  const int wq0 = w.q0 + wave * 32;  // first row of this wave
+  const int wq0 = w.q0 + (HP == 1 ? wave : wave / HP) * 32;  // first row of this wave
   const int wq_last = min(wq0 + 31, w.len - 1);
   const bool wave_live = wq0 < w.len;
   const int myq = wq0 + col;
@@ -585,7 +595,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
   Work w = decode_work<kBM, PAGED>(p, slot);
   if (!w.valid) return;
   const int n_pieces =
-      min((key_range(p, w).n_tiles + p.piece_tiles - 1) / p.piece_tiles, p.max_pieces);
+      min((key_range<kBM>(p, w).n_tiles + p.piece_tiles - 1) / p.piece_tiles, p.max_pieces);
   if (n_pieces <= 1) return;
   const float* base =
       p.partial + ((int64_t)slot * p.max_pieces * p.n_q_heads + head) * PF;
@@ -618,17 +628,27 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
 }
 
 template <int HDIM, class QT, class KVT, bool PAGED>
-void launch_paged_or_not(const PrefillParams& p, uint64_t slots, hipStream_t stream) {
+void launch_paged_or_not(PrefillParams p, uint64_t slots, hipStream_t stream) {
+  if (p.piece_tiles == 0 && p.group % 4 == 0) {
+    // four heads of one KV head per workgroup, 64 rows each
+    constexpr int bm = kBM / 4;
+    const uint64_t slots4 = (uint64_t)((p.n_tokens + bm - 1) / bm + p.n_seqs);
+    p.tile_slots = (int32_t)slots4;
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 4>),
+                       dim3((uint32_t)(slots4 * (uint64_t)(p.n_q_heads / 4))), dim3(kThreads), 0,
+                       stream, p);
+    return;
+  }
   if (p.piece_tiles > 0) {
     const uint64_t blocks = slots * (uint64_t)p.max_pieces * (uint64_t)p.n_q_heads;
-    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, true>),
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, true, 1>),
                        dim3((uint32_t)blocks), dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL((prefill_merge_kernel<HDIM, PAGED>),
                        dim3((uint32_t)(slots * (uint64_t)p.n_q_heads *
                                        (uint64_t)(kBM / merge_rows<HDIM>()))),
                        dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false>),
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 1>),
                        dim3((uint32_t)(slots * (uint64_t)p.n_q_heads)), dim3(kThreads), 0,
                        stream, p);
   }
