@@ -130,7 +130,9 @@ def test_full_parity(case):
 # ---------------------------------------------- small-shape grid (packed)
 GRID_LENGTHS = [1, 2, 63, 64, 65, 127, 128, 129, 257, 0, 1, 200]
 GRID_WINDOWS = [0, 1, 2, 63, 64, 65, 127, 128, 129, 256, 257, 258]
-GRID_HEADS = [(1, 1), (4, 1), (32, 1), (8, 8), (32, 8)]
+# (query heads, KV heads): groups of 1, 2 and 6 run one head per workgroup;
+# groups of 4, 8, 12 and 32 run four heads of a KV head per workgroup
+GRID_HEADS = [(1, 1), (4, 1), (32, 1), (8, 8), (32, 8), (12, 1), (16, 2), (6, 3)]
 GRID_SCALES = [1 / math.sqrt(128), 0.0, 1.0, -0.3]
 
 
@@ -251,6 +253,28 @@ def test_deterministic_bitwise():
     a = run_gpu(inp, 32, 1, 128, w.attn_scale, 0).clone()
     b = run_gpu(inp, 32, 1, 128, w.attn_scale, 0)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("window", [0, 70])
+def test_head_packing_matches_single_heads_bitwise(window):
+    """Four query heads of one KV head run in one workgroup (64 rows each);
+    each head alone runs 256 rows of one head.  Every row meets the same
+    key tiles in the same order, so the outputs agree bit for bit."""
+    w = workloads.custom("pack", [300, 64, 1, 191], 8, 2, seed=61)
+    _announce(f"{w.name}_w{window}")
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    cu = inp["cu_seqlens"].to(dev)
+    packed = torch.empty(q.shape[0], 8, 128, dtype=torch.bfloat16, device=dev)
+    binding.attn_prefill(q, k, v, packed, cu, 8, 2, 128, w.attn_scale, window)
+    single = torch.empty_like(packed)
+    for h in range(8):
+        g = h // 4
+        binding.attn_prefill(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], single[:, h:h + 1],
+                             cu, 1, 1, 128, w.attn_scale, window)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, single)
 
 
 def test_malformed_offsets_stay_in_bounds():
