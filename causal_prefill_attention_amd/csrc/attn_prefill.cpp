@@ -55,11 +55,25 @@ struct Extent {
   uintptr_t lo, hi;
 };
 
+// Elements from a tensor's first to one past its last element,
+// (T - 1) * token_stride + (H - 1) * head_stride + d, or -1 if that does not
+// fit in int64.
+int64_t span_elems(int64_t T, int64_t ts, int64_t H, int64_t hs, int64_t d) {
+  int64_t a, b, s;
+  if (__builtin_mul_overflow(T - 1, ts, &a) || __builtin_mul_overflow(H - 1, hs, &b) ||
+      __builtin_add_overflow(a, b, &s) || __builtin_add_overflow(s, d, &s))
+    return -1;
+  return s;
+}
+
 Extent extent_of(const attn_tensor* t, int32_t n_heads, int32_t head_dim) {
-  const int64_t last = (t->n_tokens - 1) * t->token_stride +
-                       (int64_t)(n_heads - 1) * t->head_stride + head_dim;
   const uintptr_t lo = reinterpret_cast<uintptr_t>(t->data);
-  return {lo, lo + (uintptr_t)(last * elem_bytes(t->dtype))};
+  const int64_t span =
+      span_elems(t->n_tokens, t->token_stride, n_heads, t->head_stride, head_dim);
+  int64_t bytes;
+  if (span < 0 || __builtin_mul_overflow(span, elem_bytes(t->dtype), &bytes))
+    return {lo, UINTPTR_MAX};  // (check_tensor rejects such tensors first)
+  return {lo, lo + (uintptr_t)bytes};
 }
 
 bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
@@ -83,6 +97,13 @@ int check_tensor(const attn_tensor* t, const char* what, int32_t n_heads, int32_
   // Head vectors must not overlap: token-major or head-major nesting.
   const int64_t T = t->n_tokens, H = n_heads, d = head_dim;
   const int64_t ts = t->token_stride, hs = t->head_stride;
+  // (once the span fits in int64, every product and sum below does too)
+  const int64_t span = span_elems(T, ts, H, hs, d);
+  int64_t span_bytes;
+  if (span < 0 || __builtin_mul_overflow(span, (int64_t)elem_bytes(t->dtype), &span_bytes))
+    return fail(ATTN_ERR_INVALID_ARG,
+                "%s: strides (token %lld, head %lld) put the tensor past the address range",
+                what, (long long)ts, (long long)hs);
   const bool token_major = (H == 1 || hs >= d) && (T == 1 || ts >= (H - 1) * hs + d);
   const bool head_major = (T == 1 || ts >= d) && (H == 1 || hs >= (T - 1) * ts + d);
   if (!token_major && !head_major)
@@ -92,7 +113,8 @@ int check_tensor(const attn_tensor* t, const char* what, int32_t n_heads, int32_
   const int64_t eb = elem_bytes(t->dtype);
   if ((reinterpret_cast<uintptr_t>(t->data) & 15u) != 0)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: data pointer is not 16-byte aligned", what);
-  if ((ts * eb) % 16 != 0 || (hs * eb) % 16 != 0)
+  // (unsigned products: the residue mod 16 survives wrap-around)
+  if (((uint64_t)ts * (uint64_t)eb) % 16 != 0 || ((uint64_t)hs * (uint64_t)eb) % 16 != 0)
     return fail(ATTN_ERR_UNSUPPORTED, "%s: strides are not multiples of 16 bytes", what);
   return ATTN_OK;
 }
@@ -741,8 +763,8 @@ int attn_decode_ws(const attn_tensor* q, const attn_tensor* k, const attn_tensor
 
 size_t attn_decode_workspace_size(int64_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
                                   int32_t head_dim) {
-  if (n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 ||
-      head_dim != 128)
+  if (n_seqs < 1 || n_seqs > INT32_MAX || n_q_heads < 1 || n_kv_heads < 1 ||
+      n_q_heads % n_kv_heads != 0 || head_dim != 128)
     return 0;
   const int64_t units = decode_units(n_seqs, n_q_heads, n_kv_heads);
   const int n_splits = decode_preferred_splits(units);
@@ -841,8 +863,10 @@ int attn_prefill_ex_ws(const attn_tensor* q, const attn_tensor* k, const attn_te
 size_t attn_prefill_workspace_size(int64_t n_tokens_q, int64_t max_keys, int32_t n_seqs,
                                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim_qk,
                                    int32_t head_dim_v, int32_t sliding_window) {
-  if (n_tokens_q < 1 || max_keys < 0 || n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 ||
-      n_q_heads % n_kv_heads != 0 || sliding_window < 0)
+  // (token counts beyond int32 offsets are outside every entry point's contract)
+  if (n_tokens_q < 1 || n_tokens_q > INT32_MAX || max_keys < 0 || max_keys > INT32_MAX ||
+      n_seqs < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 ||
+      sliding_window < 0)
     return 0;
   const SplitPlan sp = plan_prefill_split(n_tokens_q, max_keys, n_seqs, n_q_heads, head_dim_qk,
                                           head_dim_v, sliding_window);
