@@ -435,7 +435,8 @@ def test_decode_ws_paged_page_size_checked():
 
 
 @pytest.mark.parametrize("args", [(0, 32, 1, 128), (4, 32, 1, 64), (4, 30, 8, 128),
-                                  (4, 0, 1, 128), (-1, 32, 1, 128)])
+                                  (4, 0, 1, 128), (-1, 32, 1, 128),
+                                  ((1 << 31), 32, 1, 128), ((1 << 63) - 1, 32, 8, 128)])
 def test_decode_workspace_size_is_zero_outside_the_contract(args):
     assert B.decode_workspace_size(*args) == 0
 
@@ -540,7 +541,10 @@ def test_prefill_ws_unsupported_pairs_rejected_like_ex():
                                   (100, -1, 1, 4, 1, 128, 128, 0),
                                   (100, 100, 1, 4, 1, 128, 128, -1),
                                   (8192, 8192, 1, 4, 1, 320, 256, 0),
-                                  (8192, 8192, 1, 4, 1, 256, 256, 0)])
+                                  (8192, 8192, 1, 4, 1, 256, 256, 0),
+                                  ((1 << 31), 8192, 1, 4, 1, 128, 128, 0),
+                                  (8192, (1 << 31), 1, 4, 1, 128, 128, 0),
+                                  ((1 << 63) - 1, (1 << 63) - 1, 1, 4, 1, 128, 128, 0)])
 def test_prefill_workspace_size_is_zero_outside_the_split(args):
     # bad shapes, and head sizes without a split (also zero with no GPU)
     assert B.prefill_workspace_size(*args) == 0
