@@ -1135,3 +1135,67 @@ def test_ex_same_head_sizes_match_attn_prefill_bitwise():
                             inp["cu_seqlens"].to(dev), 8, 2, 256, 256, w.attn_scale, 0)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ graph capture
+def test_graph_capture_replays_match_eager():
+    """Every call is launches only (no allocation, host sync or memset), so
+    it can be captured in a HIP graph: a packed GQA prefill, a prefill whose
+    keys are split through a workspace and a split decode in one graph,
+    replayed three times on new inputs written eagerly between replays, each
+    replay equal bit for bit to eager calls on the same inputs."""
+    dev = torch.device("cuda:0")
+    _announce("graph_capture")
+    gen = torch.Generator(device="cpu").manual_seed(91)
+
+    def randn(*shape, dtype=torch.bfloat16):
+        return torch.randn(*shape, generator=gen).to(dtype).to(dev)
+
+    # packed GQA prefill (four heads of a KV head per workgroup)
+    lens_a = [300, 129, 64]
+    cu_a = torch.tensor([0, 300, 429, 493], dtype=torch.int32, device=dev)
+    qa, ka, va = randn(493, 8, 128), randn(493, 2, 128), randn(493, 2, 128)
+    # one long sequence on 2 query heads: keys split across workgroups
+    cu_b = torch.tensor([0, 3000], dtype=torch.int32, device=dev)
+    qb, kb, vb = randn(3000, 2, 128), randn(3000, 1, 128), randn(3000, 1, 128)
+    ws_b_bytes = binding.prefill_workspace_size(3000, 3000, 1, 2, 1, 128, 128, 0)
+    assert ws_b_bytes > 0
+    ws_b = torch.full((ws_b_bytes,), 0xFF, dtype=torch.uint8, device=dev)
+    # decode: 4 sequences of 2000 keys, 32 query heads on 8 KV heads, split
+    cu_c = torch.tensor([0, 2000, 4000, 6000, 8000], dtype=torch.int32, device=dev)
+    qc, kc, vc = randn(4, 32, 128), randn(8000, 8, 128), randn(8000, 8, 128)
+    ws_c = binding.decode_workspace(4, 32, 8, 128, device=dev)
+    assert ws_c is not None and ws_c.numel() > 0
+    scale = 1 / math.sqrt(128)
+
+    outs = [torch.empty(493, 8, 128, dtype=torch.bfloat16, device=dev),
+            torch.empty(3000, 2, 128, dtype=torch.bfloat16, device=dev),
+            torch.empty(4, 32, 128, dtype=torch.bfloat16, device=dev)]
+
+    def calls(o):
+        binding.attn_prefill(qa, ka, va, o[0], cu_a, 8, 2, 128, scale, 0)
+        binding.attn_prefill_ex(qb, kb, vb, o[1], cu_b, 2, 1, 128, 128, scale, 0,
+                                workspace=ws_b)
+        binding.attn_decode(qc, kc, vc, o[2], cu_c, 32, 8, 128, scale, 0, workspace=ws_c)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(outs)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(outs)
+    for rep in range(3):
+        for t in (qa, ka, qb, vb, qc, vc):  # new inputs, written eagerly
+            t.copy_(randn(*t.shape))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        want = [torch.empty_like(o) for o in outs]
+        calls(want)
+        torch.cuda.synchronize()
+        for name, g, w in zip(("prefill", "prefill_split", "decode_split"), got, want):
+            assert torch.equal(g, w), f"replay {rep}: {name} differs from the eager call"
