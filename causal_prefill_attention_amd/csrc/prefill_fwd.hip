@@ -1,6 +1,7 @@
 // Causal / sliding-window prefill attention forward for gfx950 (CDNA4).
 //
-// What is computed (one workgroup = one query tile of one query head):
+// What is computed (one workgroup = one query tile of one query head, or
+// of four query heads that share a KV head):
 //   out[i,h] = sum_j softmax_j(scale * q[i,h] . k[j,g]) v[j,g],
 //   j visible iff j <= i (causal bound kv_end = min(q_pos + 1, seq_len), atlas
 //   PR #69 fused MLA prefill) and, for a window W > 0, j >= i - W + 1 (the W
@@ -15,7 +16,8 @@
 //
 // Design (ours, for CDNA4 -- the pages' GB10 / M40 kernels are prior art):
 //   * 8 waves per workgroup, two per SIMD, 32 query rows per wave, 256 rows
-//     per workgroup, 64-key tiles.  The waves form two groups (A = waves 0-3,
+//     per workgroup (256 of one head, or 64 of each of four heads sharing a
+//     KV head), 64-key tiles.  The waves form two groups (A = waves 0-3,
 //     B = waves 4-7; wave w and w + 4 share a SIMD) that run in anti-phase:
 //     in each barrier-delimited slot one group issues its matrix work
 //     [P(j-1) V(j-1), then S(j) = K(j) Q^T] while the other runs the softmax
