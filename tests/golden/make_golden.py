@@ -134,6 +134,30 @@ EXAMPLES += [
         [[[0.75]], [[2.0]]]),
 ]
 
+# Separate q/k and v head sizes (the absorbed MLA prefill of the atlas PR #69
+# page: 320-wide q/k rows, 256-wide values): the scores use the d_qk columns
+# of q and k, the output has the d_v columns of v.
+
+EXAMPLES += [
+    ex("split_head_sizes_dqk2_dv3",
+       "d_qk = 2, d_v = 3: row 0 sees key 0 only -> v0 = [4, 0, -8]; row 1 "
+       "scores [q1.k0, q1.k1] = [0, (ln3 - 1) + 0.5*2] = [0, ln3] -> "
+       "weights [1/4, 3/4] -> [1, 3, 4]",
+       [0, 2], 1, 1, 1.0, 0,
+       [[[2.0, -7.0]], [[1.0, 0.5]]], [[[0.0, 0.0]], [[LN3 - 1.0, 2.0]]],
+       [[[4.0, 0.0, -8.0]], [[0.0, 4.0, 8.0]]],
+       [[[4.0, 0.0, -8.0]], [[1.0, 3.0, 4.0]]]),
+    ex("split_head_sizes_dqk3_dv1_gqa",
+       "d_qk = 3, d_v = 1, 2 Q heads on 1 KV head: head 0 row 1 scores "
+       "[0, ln2] -> [1/3, 2/3] -> (6 + 2*9)/3 = 8; head 1 row 1 scores "
+       "[0, -ln2] -> [2/3, 1/3] -> (2*6 + 9)/3 = 7; row 0 -> v0 = 6",
+       [0, 2], 2, 1, 1.0, 0,
+       [[[1.0, 1.0, 1.0], [3.0, 3.0, 3.0]], [[1.0, 0.0, 0.0], [0.0, -1.0, 0.0]]],
+       [[[0.0, 0.0, -5.0]], [[LN2, LN2, 0.0]]],
+       [[[6.0]], [[9.0]]],
+       [[[6.0], [6.0]], [[8.0], [7.0]]]),
+]
+
 # Paged KV: key position j of sequence s is slot j % page_size of page
 # block_table[s][j // page_size] (atlas PR #69, paged MLA prefill: a page
 # table lookup per position).

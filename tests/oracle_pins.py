@@ -107,6 +107,58 @@ def pin_bruteforce(mod):
             assert err_r <= 1e-12, f"brute case {case_id} rows: max err {err_r}"
 
 
+# Separate q/k and v head sizes (the absorbed MLA prefill of the atlas PR #69
+# page attends with 320-wide q/k rows and extracts 256-wide values): the
+# scores use d_qk columns, the output has d_v columns.  Both d_v < d_qk and
+# d_v > d_qk occur, so that neither width can stand in for the other.
+BRUTE_CASES_DV = [
+    # lengths, hq, hkv, d_qk, d_v, window, scale
+    ([5], 1, 1, 5, 3, 0, 0.8),
+    ([4, 0, 7], 4, 2, 3, 5, 2, 0.6),
+    ([9, 1], 2, 1, 8, 2, 0, -0.4),
+    ([6], 4, 1, 2, 7, 4, 1.1),
+]
+
+CHUNK_CASES_DV = [
+    # (q lengths, kv lengths), hq, hkv, d_qk, d_v, window, scale
+    (([2, 3], [6, 3]), 2, 1, 5, 3, 0, 0.7),
+    (([1], [8]), 4, 2, 2, 6, 3, 0.5),
+]
+
+
+def pin_bruteforce_split_head_sizes(mod):
+    for case_id, (lengths, hq, hkv, dq, dv, w, scale) in enumerate(BRUTE_CASES_DV):
+        rng = np.random.default_rng(500 + case_id)
+        t = sum(lengths)
+        q = rng.standard_normal((t, hq, dq))
+        k = rng.standard_normal((t, hkv, dq))
+        v = rng.standard_normal((t, hkv, dv))
+        cu = _cu(lengths)
+        want = np.array(brute_attention(q.tolist(), k.tolist(), v.tolist(), cu,
+                                        hq, hkv, scale, w)).reshape(t, hq, dv)
+        got = mod.attention_varlen(q, k, v, cu, hq, hkv, scale, w, workers=1)
+        assert got.shape == (t, hq, dv), f"dv case {case_id}: shape {got.shape}"
+        err = np.max(np.abs(got - want)) if got.size else 0.0
+        assert err <= 1e-12, f"dv case {case_id}: max err {err}"
+        rows = [(tok, h) for tok in range(t) for h in range(hq)]
+        if rows:
+            got_r = mod.attention_rows(q, k, v, cu, hq, hkv, scale, w, rows)
+            want_r = np.array([want[tok, h] for tok, h in rows])
+            assert np.max(np.abs(got_r - want_r)) <= 1e-12, f"dv case {case_id} rows"
+    for case_id, ((lq, lk), hq, hkv, dq, dv, w, scale) in enumerate(CHUNK_CASES_DV):
+        rng = np.random.default_rng(550 + case_id)
+        q = rng.standard_normal((sum(lq), hq, dq))
+        k = rng.standard_normal((sum(lk), hkv, dq))
+        v = rng.standard_normal((sum(lk), hkv, dv))
+        cq, ck = _cu(lq), _cu(lk)
+        want = np.array(brute_attention_chunked(
+            q.tolist(), k.tolist(), v.tolist(), cq, ck, hq, hkv, scale, w)
+        ).reshape(q.shape[0], hq, dv)
+        got = mod.attention_chunked(q, k, v, cq, ck, hq, hkv, scale, w, workers=1)
+        assert got.shape == want.shape, f"dv chunk case {case_id}: shape {got.shape}"
+        assert np.max(np.abs(got - want)) <= 1e-12, f"dv chunk case {case_id}"
+
+
 def pin_rows_sum_to_one(mod):
     rng = np.random.default_rng(7)
     for n, w in ((1, 0), (17, 0), (40, 3), (40, 40)):
@@ -384,6 +436,7 @@ def pin_decode_is_the_last_prefill_row(mod):
 ALL_PINS = [
     pin_golden,
     pin_bruteforce,
+    pin_bruteforce_split_head_sizes,
     pin_rows_sum_to_one,
     pin_window_zero_equals_long_window,
     pin_window_one_returns_v,

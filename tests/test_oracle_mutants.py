@@ -147,6 +147,32 @@ def _paged_slot_transposed(mod):
     return gather_pages
 
 
+def _values_cut_to_qk_width(mod):
+    # forms P . V with only as many value columns as q/k have (the head size
+    # of q taken for v's as well), zero beyond
+    base = mod.attention_head
+
+    def attention_head(q_h, k_g, v_g, scale, window, q_offset=None):
+        v = np.array(v_g, dtype=np.float64)
+        dq = np.shape(q_h)[1]
+        v[:, dq:] = 0.0
+        return base(q_h, k_g, v, scale, window, q_offset)
+    return attention_head
+
+
+def _scores_over_value_width(mod):
+    # forms the scores over the first d_v columns of q and k (the head size
+    # of v taken for q/k's as well)
+    base = mod.attention_head
+
+    def attention_head(q_h, k_g, v_g, scale, window, q_offset=None):
+        dv = np.shape(v_g)[1]
+        q = np.asarray(q_h, dtype=np.float64)[:, :dv]
+        k = np.asarray(k_g, dtype=np.float64)[:, :dv]
+        return base(q, k, v_g, scale, window, q_offset)
+    return attention_head
+
+
 MUTANTS = {
     "causal_excludes_self": ("visibility", _vis(
         lambda i, j, w: (j < i) | ((i == 0) & (j == 0)) if w == 0 else
@@ -172,6 +198,8 @@ MUTANTS = {
     "chunk_sees_only_its_own_keys": ("attention_chunked", None),
     "paged_table_ignored": ("gather_pages", None),
     "paged_page_and_slot_swapped": ("gather_pages", None),
+    "values_cut_to_qk_width": ("attention_head", None),
+    "scores_over_value_width": ("attention_head", None),
 }
 
 
@@ -191,5 +219,9 @@ def test_mutant_is_caught(name):
         repl = _paged_wrong_slot(mod)
     if name == "paged_page_and_slot_swapped":
         repl = _paged_slot_transposed(mod)
+    if name == "values_cut_to_qk_width":
+        repl = _values_cut_to_qk_width(mod)
+    if name == "scores_over_value_width":
+        repl = _scores_over_value_width(mod)
     setattr(mod, attr, repl)
     assert failing_pins(mod), f"mutant {name} passed every pin"
