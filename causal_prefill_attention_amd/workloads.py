@@ -12,7 +12,10 @@ Recipe (the same for every workload):
   ``standard_normal`` in float64, each shaped ``[T, heads, head_dim]``, then
   the K outlier positions (``choice`` without replacement over the flat K,
   ``floor(frac * K.size)`` of them), which are multiplied by the outlier
-  factor in float64.
+  factor in float64; a workload with outlier *channels* instead draws, per
+  KV head, ``k_outlier_channels`` distinct head-dim indices (``choice``
+  without replacement over ``head_dim``) and multiplies that column of
+  every token by the same factor.
 * The float64 draws are narrowed to the storage dtype by torch's CPU cast
   (round to nearest even).
 
@@ -59,6 +62,7 @@ class Workload:
     random_lengths: Optional[Tuple[int, int, int]] = None  # (n_seqs, lo, hi)
     k_outlier_frac: float = 0.0
     k_outlier_mult: float = 30.0
+    k_outlier_channels: int = 0  # whole K channels (per KV head) scaled, every token
     scale: Optional[float] = None  # None -> 1/sqrt(head_dim)
     history: Optional[Tuple[int, ...]] = None  # KV history per sequence (chunked)
     decode: bool = False  # one query per sequence, run through the decode kernel
@@ -81,6 +85,8 @@ class Workload:
             "q_dtype": self.q_dtype,
             "kv_dtype": self.kv_dtype,
             "k_outlier_frac": self.k_outlier_frac,
+            **({"k_outlier_channels": self.k_outlier_channels}
+               if self.k_outlier_channels else {}),
             "scale": self.attn_scale,
             **({"history": list(self.history)} if self.history else {}),
             **({"decode": True} if self.decode else {}),
@@ -112,6 +118,12 @@ WORKLOADS: Dict[str, Workload] = {
     "long_8192tok_32q1kv_outliers": Workload(
         "long_8192tok_32q1kv_outliers", 4, (8192,), 32, 1, _D,
         k_outlier_frac=0.01, scale=_SCALE),
+    # the long prefill with whole outlier channels: round(1% of 128) = 1 K
+    # channel per KV head scaled by 30 for every token (the peakiest
+    # softmax that "1% of K entries x30 (outlier channels)" admits)
+    "long_8192tok_32q1kv_outlier_channel": Workload(
+        "long_8192tok_32q1kv_outlier_channel", 4, (8192,), 32, 1, _D,
+        k_outlier_channels=1, scale=_SCALE),
     # one GPU's share of the long prefill under 8-way head sharding
     "long_8192tok_4q1kv_outliers_share": Workload(
         "long_8192tok_4q1kv_outliers_share", 4, (8192,), 4, 1, _D,
@@ -161,12 +173,14 @@ def custom(name: str, lengths: Sequence[int], n_q_heads: int, n_kv_heads: int,
            head_dim: int = _D, window: int = 0, q_dtype: str = "bf16",
            kv_dtype: str = "bf16", seed: int = 0, scale: Optional[float] = None,
            k_outlier_frac: float = 0.0,
-           history: Optional[Sequence[int]] = None) -> Workload:
+           history: Optional[Sequence[int]] = None,
+           k_outlier_channels: int = 0) -> Workload:
     """A test-sized workload with explicit lengths (and KV histories)."""
     return Workload(name, seed, tuple(int(x) for x in lengths), n_q_heads,
                     n_kv_heads, head_dim, window=window, q_dtype=q_dtype,
                     kv_dtype=kv_dtype, scale=scale,
                     k_outlier_frac=k_outlier_frac,
+                    k_outlier_channels=k_outlier_channels,
                     history=None if history is None else tuple(int(x) for x in history))
 
 
@@ -216,6 +230,10 @@ def make_inputs(w: Workload) -> Dict[str, object]:
         idx = rng.choice(k64.size, size=n_out, replace=False)
         flat = k64.reshape(-1)
         flat[idx] *= w.k_outlier_mult
+    if w.k_outlier_channels > 0 and k64.size > 0:
+        for g in range(w.n_kv_heads):
+            ch = rng.choice(d, size=w.k_outlier_channels, replace=False)
+            k64[:, g, ch] *= w.k_outlier_mult
     q = torch.from_numpy(q64).to(_TORCH_DTYPES[w.q_dtype])
     k = torch.from_numpy(k64).to(_TORCH_DTYPES[w.kv_dtype])
     v = torch.from_numpy(v64).to(_TORCH_DTYPES[w.kv_dtype])

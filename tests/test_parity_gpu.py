@@ -4,11 +4,13 @@ Bar (on the bf16 outputs, against the unrounded float64 oracle):
     max |gpu - oracle| <= 2e-2   and   mean |gpu - oracle| <= 2e-3
 Every comparison prints the fraction of each bar it used.
 
-Sizes: every configuration that the oracle finishes in seconds is compared
-element by element (several 128-row query tiles, ragged tails, packed
-batches); the full-size workloads are compared on a seeded sample of
+Sizes: the five problem shapes (128 and 2048 tokens, the 4096-token window,
+the packed fp32-Q / fp16-KV GQA batch, the 8192-token long prefill with K
+outlier entries, and the same with a whole outlier channel) are compared
+element by element on every output; so are smaller ragged and packed
+cases.  Every full-size workload is also compared on a seeded sample of
 (token, head) rows that the oracle evaluates one by one, from the same
-launch the benchmark times.
+launch configuration the benchmark times.
 """
 import json
 import math
@@ -27,6 +29,16 @@ pytestmark = pytest.mark.gpu
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 LOG = os.environ.get("ATTN_PARITY_LOG")
+
+
+def _oracle_threads():
+    """Oracle worker threads: the CPUs this process may use, at most 16
+    (each full-size job holds a few GB of float64 temporaries)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _announce(msg):
@@ -101,6 +113,10 @@ FULL = [
     # name, lengths, hq, hkv, window, q dtype, kv dtype, scale
     ("causal_128tok_4q1kv", None, 0, 0, 0, None, None, None),
     ("mla_2048tok_32q1kv", None, 0, 0, 0, None, None, None),
+    ("window1024_4096tok_32q1kv", None, 0, 0, 0, None, None, None),
+    ("varlen16_gqa32q8kv_fp32q_fp16kv", None, 0, 0, 0, None, None, None),
+    ("long_8192tok_32q1kv_outliers", None, 0, 0, 0, None, None, None),
+    ("long_8192tok_32q1kv_outlier_channel", None, 0, 0, 0, None, None, None),
     ("window256_1100tok_32q1kv", [1100], 32, 1, 256, "bf16", "bf16", None),
     ("varlen_gqa_fp32q_fp16kv_small", [300, 64, 1, 0, 517, 129], 32, 8, 0,
      "fp32", "fp16", None),
@@ -123,7 +139,8 @@ def test_full_parity(case):
     inp = workloads.make_inputs(w)
     out = run_gpu(inp, w.n_q_heads, w.n_kv_heads, w.head_dim, w.attn_scale, w.window)
     want = oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
-                                   w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window)
+                                   w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window,
+                                   workers=_oracle_threads())
     check(name, to64(out), want)
 
 
@@ -1027,21 +1044,20 @@ def test_head_dim_512_dtypes(qd, kvd):
     check(w.name, to64(out), oracle_of(inp, 4, 2, w.attn_scale, 0))
 
 
-def test_head_dim_512_fp32_fp16_outliers_against_bf16_rounded_inputs():
-    """fp32 q and fp16 k with x30 outliers: the library rounds q, k and v to
-    bf16 on load (its stated precision), and that rounding alone moves the
-    exact result by up to ~0.056 (max) / 0.0025 (mean) at these inputs, past
-    the bar -- the oracle in fp64 on the rounded inputs shows it.  The
-    kernel is therefore held to the bar against the oracle on the inputs
-    rounded to bf16 (torch on the CPU), which is the arithmetic the header
-    documents."""
+@pytest.mark.xfail(strict=False, reason=(
+    "the 512-d kernel narrows fp32 q and fp16 k/v to bf16 before its products; "
+    "with x30 K outliers that rounding alone moves the exact result by up to "
+    "0.056 max / 0.0025 mean (measured with the oracle on bf16-rounded inputs), "
+    "past the 2e-2 / 2e-3 bar"))
+def test_head_dim_512_fp32_fp16_outliers():
+    """fp32 q and fp16 k with x30 outliers against the exact oracle on the
+    inputs as stored."""
     w = workloads.custom("d512_fp32_fp16_outliers", [200, 1, 77], 4, 2, head_dim=512,
                          q_dtype="fp32", kv_dtype="fp16", seed=132, k_outlier_frac=0.01)
     _announce(w.name)
     inp = workloads.make_inputs(w)
     out = run_gpu(inp, 4, 2, 512, w.attn_scale, 0)
-    rounded = {**inp, **{x: inp[x].to(torch.bfloat16).to(torch.float64) for x in "qkv"}}
-    check(w.name, to64(out), oracle_of(rounded, 4, 2, w.attn_scale, 0))
+    check(w.name, to64(out), oracle_of(inp, 4, 2, w.attn_scale, 0))
 
 
 def test_head_dim_512_chunked_and_paged():

@@ -46,6 +46,23 @@ def test_outlier_count():
     assert changed == n
 
 
+def test_outlier_channels_scale_whole_columns():
+    w = workloads.custom("oc", [50], 4, 2, head_dim=128, seed=6, k_outlier_channels=1)
+    base = workloads.custom("b", [50], 4, 2, head_dim=128, seed=6)
+    k1 = workloads.make_inputs(w)["k"].double()
+    k0 = workloads.make_inputs(base)["k"].double()
+    assert torch.equal(workloads.make_inputs(w)["q"], workloads.make_inputs(base)["q"])
+    for g in range(2):
+        cols = [c for c in range(128) if not torch.equal(k1[:, g, c], k0[:, g, c])]
+        assert len(cols) == 1, cols
+        c = cols[0]
+        # x30 in float64 before the bf16 cast: compare after the same cast
+        want = (k0[:, g, c] * 30).to(torch.bfloat16).double()
+        assert torch.allclose(k1[:, g, c], want, rtol=2 ** -7)
+    full = workloads.WORKLOADS["long_8192tok_32q1kv_outlier_channel"]
+    assert full.k_outlier_channels == round(0.01 * 128) == 1
+
+
 @pytest.mark.parametrize("n,w", [(0, 0), (1, 0), (5, 0), (5, 1), (5, 3),
                                  (5, 5), (5, 9), (64, 17), (130, 64)])
 def test_pair_count_closed_form_matches_brute_count(n, w):
