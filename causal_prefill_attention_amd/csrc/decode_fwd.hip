@@ -13,13 +13,14 @@
 // Design (ours, for CDNA4):
 //   * One workgroup per (sequence, KV head, block of 32 query heads): the
 //     query heads that share a KV head are the 32 columns of the MFMA, so
-//     Sᵀ = K Qᵀ and Oᵀ += Vᵀ Pᵀ run on v_mfma_f32_32x32x16_bf16 exactly as
-//     in the prefill kernel, with heads in place of query tokens (MQA with
+//     Sᵀ = K Qᵀ and Oᵀ += Vᵀ Pᵀ run on the 32x32x16 MFMA of the K/V storage
+//     type (bf16 or fp16, K and V as stored) exactly as in the prefill
+//     kernel, with heads in place of query tokens (MQA with
 //     32 query heads fills the columns; smaller groups leave some empty).
 //   * Four waves, one per SIMD, split the key range into contiguous slices
 //     of 64-key tiles and stream their slice independently: each tile is
-//     loaded with coalesced 16-byte loads into registers one tile ahead,
-//     converted to bf16 and stored into the wave's own LDS slice with the
+//     loaded with coalesced 16-byte loads into registers one tile ahead and
+//     stored into the wave's own LDS slice with the
 //     16-byte chunks of row r at position (chunk ^ (r & 15)); K operands are
 //     read back row-wise, Vᵀ operands with the transposing LDS read
 //     ds_read_b64_tr_b16 (four keys of one column per lane per read).
@@ -63,8 +64,10 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   static_assert(DBLK == kDWaves, "one output block per wave");
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
+  typedef typename OpOf<KVT>::T OP;  // operand type of both products
+  typedef typename OP::v8 opv8;
 
-  // Per wave: K tile then V tile (bf16, rows of HDIM, chunks swizzled).
+  // Per wave: K tile then V tile (rows of HDIM, chunks swizzled).
   // After the key loop the same memory holds the merge buffers.
   __shared__ __attribute__((aligned(16))) uint16_t smem[kDWaves * 2 * TILE];
 
@@ -181,8 +184,8 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
     for (int i = 0; i < LOADS; ++i) {
       const int row = i * (kDWave / CPR) + lane / CPR;
       const int pos = (lane % CPR) ^ (row & 15);
-      *reinterpret_cast<u32x4_t*>(kt + row * HDIM + 8 * pos) = kv_to_bf16(KVT(), kr[i]);
-      *reinterpret_cast<u32x4_t*>(vt + row * HDIM + 8 * pos) = kv_to_bf16(KVT(), vr[i]);
+      *reinterpret_cast<u32x4_t*>(kt + row * HDIM + 8 * pos) = kv_to_op(OP(), KVT(), kr[i]);
+      *reinterpret_cast<u32x4_t*>(vt + row * HDIM + 8 * pos) = kv_to_op(OP(), KVT(), vr[i]);
     }
   };
 
@@ -193,7 +196,6 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   float m_run = -INFINITY;
   float l_run = 0.f;
   const float cmul = p.score_mult;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // first tile in flight before Q, so that the two latencies overlap
   if (t_begin < t_end) gload(kv_start + t_begin * kDBN);
@@ -201,11 +203,11 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
   // ---- Qᵀ operand: lane holds q[s, head, 16c + 8*half .. +7], zeroed for a
   // column past the group (head is clamped to a real head, so every load is
   // in bounds and none waits behind a branch)
-  bf16x8_t qf[DCH];
+  opv8 qf[DCH];
   {
     const qelem* qp = static_cast<const qelem*>(p.q) + (int64_t)s * p.q_ts +
                       (int64_t)head * p.q_hs;
-    load_q_operand<DCH>(qp, half, hvalid ? p.q_mult : 0.f, qf);
+    load_q_op<DCH, OP>(qp, half, hvalid ? p.q_mult : 0.f, qf);
   }
 
   for (int t = t_begin; t < t_end; ++t) {
@@ -225,8 +227,8 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
 #pragma unroll
       for (int c = 0; c < DCH; ++c) {
         const int pos = (2 * c + half) ^ (row & 15);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + row * HDIM + 8 * pos);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc[kb], 0, 0, 0);
+        const opv8 a = *reinterpret_cast<const opv8*>(kt + row * HDIM + 8 * pos);
+        sc[kb] = OP::mfma(a, qf[c], sc[kb]);
       }
     }
     // mask the window start and the key count (first and last tiles only)
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
           if (key < kv_lo || key >= L) sc[kb][r] = -INFINITY;
         }
     }
-    // online softmax (lazy max, base 2) into the bf16 Pᵀ operand
+    // online softmax (lazy max, base 2) into the Pᵀ operand
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
     const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
     m_run = m_new;
-    bf16x8_t pf[4];
+    opv8 pf[4];
     float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
@@ -261,11 +263,11 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
       for (int e = 0; e < 4; ++e) {
         const float p0 = fast_exp2(fmaf(sc[kq >> 1][8 * (kq & 1) + 2 * e], cmul, neg_mc));
         const float p1 = fast_exp2(fmaf(sc[kq >> 1][8 * (kq & 1) + 2 * e + 1], cmul, neg_mc));
-        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        const typename OP::v2 pb = OP::cvt2(p0, p1);
         u[e] = __builtin_bit_cast(uint32_t, pb);
-        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
+        l4[e] = OP::sum2(pb, l4[e]);
       }
-      pf[kq] = __builtin_bit_cast(bf16x8_t, u);
+      pf[kq] = __builtin_bit_cast(opv8, u);
     }
     l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
     if (any) {
@@ -298,8 +300,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
         u[1] = __builtin_bit_cast(u32x2_t, part[0])[1];
         u[2] = __builtin_bit_cast(u32x2_t, part[1])[0];
         u[3] = __builtin_bit_cast(u32x2_t, part[1])[1];
-        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u), pf[kq],
-                                                       o[c], 0, 0, 0);
+        o[c] = OP::mfma(__builtin_bit_cast(opv8, u), pf[kq], o[c]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -13,6 +13,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -52,34 +53,76 @@ __device__ __forceinline__ void load8f(const float* p, float* f) {
   }
 }
 
-// The Qᵀ MFMA operand of one lane: chunk c holds the eight elements at
-// 16c + 8*half of the query row at qp, times mult (+-1 carries the sign of
-// the scale, 0 blanks a lane without a query; qp must still point at a real
-// row).  Every load is issued before any is used and none sits behind a
-// branch, so the row costs one memory latency.
-template <int DCH, class T>
-__device__ __forceinline__ void load_q_operand(const T* qp, int half, float mult,
-                                               bf16x8_t* qf) {
+// ------------------------------------------------------ MFMA operand types
+// The matrix products run in the K/V storage type: bf16 K/V on the bf16
+// MFMA, fp16 K/V on the fp16 MFMA, so that keys and values enter both
+// products exactly as stored (the pages keep K/V in FP16 and compute in
+// FP32: m40-llm AGENTS.md "Project Snapshot").  Q and the probabilities P
+// are rounded (to nearest even) to that type; accumulation is fp32.
+struct OpBF16 {
+  typedef bf16x8_t v8;
+  typedef bf16x2_t v2;
+  static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v2 cvt2(float a, float b) {
+    return __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  }
+  // acc + x.x + x.y
+  static __device__ __forceinline__ float sum2(v2 x, float acc) {
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
+  }
+};
+
+struct OpFP16 {
+  typedef f16x8_t v8;
+  typedef f16x2_t v2;
+  static __device__ __forceinline__ f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v2 cvt2(float a, float b) {
+    return __builtin_convertvector((f32x2_t){a, b}, f16x2_t);
+  }
+  static __device__ __forceinline__ float sum2(v2 x, float acc) {
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(x, ones, acc, false);
+  }
+};
+
+// Operand type of each K/V storage type.
+template <class KVT> struct OpOf;
+template <> struct OpOf<BF16> { typedef OpBF16 T; };
+template <> struct OpOf<FP16> { typedef OpFP16 T; };
+
+// Raw 16-byte K/V chunk -> eight operand elements: the identity when the
+// operand type is the storage type.
+__device__ __forceinline__ u32x4_t kv_to_op(OpBF16, BF16, u32x4_t raw) { return raw; }
+__device__ __forceinline__ u32x4_t kv_to_op(OpFP16, FP16, u32x4_t raw) { return raw; }
+
+// Eight floats -> the operand register of type OP.
+template <class OP>
+__device__ __forceinline__ typename OP::v8 to_op8(const float* f, float mult) {
+  u32x4_t u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    u[e] = __builtin_bit_cast(uint32_t, OP::cvt2(f[2 * e] * mult, f[2 * e + 1] * mult));
+  return __builtin_bit_cast(typename OP::v8, u);
+}
+
+// The Qᵀ MFMA operand of one lane in operand type OP: chunk c holds the
+// eight elements at 16c + 8*half of the query row at qp, times mult (+-1
+// carries the sign of the scale, 0 blanks a lane without a query; qp must
+// still point at a real row).  Every load is issued before any is used and
+// none sits behind a branch, so the row costs one memory latency.
+template <int DCH, class OP, class T>
+__device__ __forceinline__ void load_q_op(const T* qp, int half, float mult,
+                                          typename OP::v8* qf) {
   float f[DCH][8];
 #pragma unroll
   for (int c = 0; c < DCH; ++c) load8f(qp + 16 * c + 8 * half, f[c]);
 #pragma unroll
-  for (int c = 0; c < DCH; ++c) {
-    u32x4_t u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(f[c][2 * e] * mult, f[c][2 * e + 1] * mult);
-    qf[c] = __builtin_bit_cast(bf16x8_t, u);
-  }
-}
-
-// Raw 16-byte K/V chunk -> eight bf16 (identity for bf16 storage).
-__device__ __forceinline__ u32x4_t kv_to_bf16(BF16, u32x4_t raw) { return raw; }
-__device__ __forceinline__ u32x4_t kv_to_bf16(FP16, u32x4_t raw) {
-  const f16x8_t h = __builtin_bit_cast(f16x8_t, raw);
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2((float)h[2 * i], (float)h[2 * i + 1]);
-  return r;
+  for (int c = 0; c < DCH; ++c) qf[c] = to_op8<OP>(f[c], mult);
 }
 
 // Value of the other half-wave's lane (l <-> l ^ 32) combined with ours.

@@ -16,7 +16,7 @@
 //     columns [128w, 128w + 128) of Q, K, V and out, so waves w and w + 4 --
 //     one SIMD -- share that column slice of every K/V tile.
 //   * Per 32-key tile a wave forms partial scores Sᵀ_w = K_w Q_wᵀ from its
-//     columns (8 MFMAs, 32x32x16 bf16) and writes them to its group's LDS
+//     columns (8 MFMAs, 32x32x16 in the K/V storage type) and writes them to its group's LDS
 //     exchange; in the group's next slot every wave sums the four partials
 //     in the same order (so all four hold the same fp32 scores), runs the
 //     same online softmax, and later accumulates Oᵀ_w += Vᵀ_w Pᵀ for its 128
@@ -27,7 +27,7 @@
 //     next slot the other way round, so the matrix core of each SIMD is fed
 //     by one wave while the vector ALU works for the other.
 //   * Group A stages the K column slices and group B the V slices through
-//     registers into two LDS stages (rows of 128 bf16, 16-byte chunks of row
+//     registers into two LDS stages (rows of 128 elements, 16-byte chunks of row
 //     r at position chunk ^ (r & 15)); Vᵀ operands come from the transposing
 //     LDS read ds_read_b64_tr_b16.  LDS: 128 KiB of K/V stages and 32 KiB of
 //     exchange.
@@ -65,8 +65,10 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   constexpr int LOADS = kGBN * CPR / kGWave;  // 16-byte chunks per lane per tile
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
+  typedef typename OpOf<KVT>::T OP;  // operand type of both products
+  typedef typename OP::v8 opv8;
 
-  // [stage][slice][K, V][TILE] bf16, then the exchange [group][slice][r/4][lane]
+  // [stage][slice][K, V][TILE] operand elements, then the exchange [group][slice][r/4][lane]
   __shared__ __attribute__((aligned(16))) uint16_t kvs[2 * kGSlices * 2 * TILE];
   __shared__ __attribute__((aligned(16))) f32x4_t xch[2 * kGSlices * 4 * kGWave];
 
@@ -136,12 +138,12 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
     for (int i = 0; i < LOADS; ++i) {
       const int row = i * (kGWave / CPR) + lane / CPR;
       const int pos = (lane % CPR) ^ (row & 15);
-      *reinterpret_cast<u32x4_t*>(dst + row * kGSlice + 8 * pos) = kv_to_bf16(KVT(), st_regs[i]);
+      *reinterpret_cast<u32x4_t*>(dst + row * kGSlice + 8 * pos) = kv_to_op(OP(), KVT(), st_regs[i]);
     }
   };
 
   // ---- Qᵀ operand of this wave's slice: lane holds q[myq, d0 + 16c + 8*half ..]
-  bf16x8_t qf[DCH];
+  opv8 qf[DCH];
   const qelem* const qrow = static_cast<const qelem*>(p.q) +
                             (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
                             (int64_t)head * p.q_hs + d0;
@@ -151,11 +153,10 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   f32x16_t o[DBLK];
 #pragma unroll
   for (int c = 0; c < DBLK; ++c) o[c] = (f32x16_t){};
-  bf16x8_t pf[kGKQ];
+  opv8 pf[kGKQ];
   float m_run = -INFINITY;
   float l_run = 0.f;
   const float cmul = p.score_mult;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   f32x4_t* const xg = xch + group * kGSlices * 4 * kGWave;  // this group's exchange
   f32x4_t* const xw = xg + sl * 4 * kGWave;                   // this wave's partial
 
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
 #pragma unroll
     for (int c = 0; c < DCH; ++c) {
       const int pos = (2 * c + half) ^ (col & 15);
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kt + col * kGSlice + 8 * pos);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sc, 0, 0, 0);
+      const opv8 a = *reinterpret_cast<const opv8*>(kt + col * kGSlice + 8 * pos);
+      sc = OP::mfma(a, qf[c], sc);
     }
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
@@ -200,8 +201,7 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
         u[1] = __builtin_bit_cast(u32x2_t, part[0])[1];
         u[2] = __builtin_bit_cast(u32x2_t, part[1])[0];
         u[3] = __builtin_bit_cast(u32x2_t, part[1])[1];
-        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, u), pf[kq],
-                                                       o[c], 0, 0, 0);
+        o[c] = OP::mfma(__builtin_bit_cast(opv8, u), pf[kq], o[c]);
       }
     }
   };
@@ -250,11 +250,11 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
         const float p0 = fast_exp2(fmaf(sc[8 * kq + 2 * e], cmul, neg_mc));
         const float p1 = fast_exp2(fmaf(sc[8 * kq + 2 * e + 1], cmul, neg_mc));
         // (the converted pair feeds the dot product directly; see the 128-d kernel)
-        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        const typename OP::v2 pb = OP::cvt2(p0, p1);
         u[e] = __builtin_bit_cast(uint32_t, pb);
-        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
+        l4[e] = OP::sum2(pb, l4[e]);
       }
-      pf[kq] = __builtin_bit_cast(bf16x8_t, u);
+      pf[kq] = __builtin_bit_cast(opv8, u);
     }
     l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
     if (any) {
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   // ---- prologue: K(0) stored (group A), V(0) in flight (group B), Q loaded
   // once the first tile's loads are issued
   gload(kv_start);
-  load_q_operand<DCH>(qrow, half, qmul, qf);
+  load_q_op<DCH, OP>(qrow, half, qmul, qf);
   if (group == 0) {
     lstore(0);
     if (n_tiles > 1) gload(kv_start + kGBN);

@@ -25,17 +25,20 @@
 //     vector ALU are fed by different waves.  K(j) and V(j-1) stay in LDS for
 //     both slots; group A stages the next tiles (global loads in its matrix
 //     slot, LDS stores in its softmax slot) into the other LDS buffers.
-//   * Both contractions use v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+//   * Both contractions run on the 32x32x16 MFMA of the K/V storage type
+//     (bf16 K/V: v_mfma_f32_32x32x16_bf16; fp16 K/V: ..._f16, so keys and
+//     values enter the products as stored) with fp32 accumulation; Q and P
+//     are rounded to that type.
 //     Scores are formed transposed, S^T = K Q^T (keys on the MFMA M axis,
 //     queries on N), so every lane owns one query column: the per-query max
 //     and sum reduce 16 values in-lane plus one lane-pair exchange
 //     (v_permlane32_swap), and the softmax row scale is one scalar per lane.
-//   * The S^T accumulator, rounded to bf16, is directly the B operand of
+//   * The S^T accumulator, rounded to the operand type, is directly the B operand of
 //     O^T += V^T P^T.  The key order inside each 16-key MFMA step follows the
 //     accumulator layout; V^T is written into LDS in that permuted order.
 //   * The running max moves lazily: O and l are rescaled only when a query's
 //     max grows by more than 2^kLazy (a rare wave-uniform branch); l sums the
-//     bf16-rounded probabilities with v_dot2 so it matches what P.V uses.
+//     rounded probabilities with v_dot2 so it matches what P.V uses.
 //   * Masks are applied only to tiles that straddle the diagonal or the
 //     window edge.  Every wave runs every tile of its workgroup; a tile none
 //     of its rows can see is fully masked and adds exact zeros.
@@ -78,8 +81,8 @@ constexpr float kLazy = 8.0f;
 template <int HDIM>
 struct Cfg {
   static_assert(HDIM % 32 == 0, "head_dim must be a multiple of 32");
-  static constexpr int KSTR = HDIM + 8;  // K row pitch in LDS (bf16 elements)
-  static constexpr int VSTR = kBN + 8;   // V^T row pitch in LDS (bf16 elements)
+  static constexpr int KSTR = HDIM + 8;  // K row pitch in LDS (16-bit elements)
+  static constexpr int VSTR = kBN + 8;   // V^T row pitch in LDS (16-bit elements)
   static constexpr int K_ELEMS = kBN * KSTR;
   static constexpr int V_ELEMS = HDIM * VSTR;
   static constexpr int DCH = HDIM / 16;   // MFMA k-steps of the Q.K contraction
@@ -135,7 +138,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   using C = Cfg<HDIM>;
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
-  // K stages [2][kBN][KSTR] then V^T stages [2][HDIM][VSTR] (bf16 bits).
+  typedef typename OpOf<KVT>::T OP;  // operand type of both products
+  typedef typename OP::v8 opv8;
+  // K stages [2][kBN][KSTR] then V^T stages [2][HDIM][VSTR] (operand bits).
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::K_ELEMS + 2 * C::V_ELEMS];
   uint16_t* const kstage0 = smem;
   uint16_t* const vstage0 = smem + 2 * C::K_ELEMS;
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int mypos = hist + myq;  // key position of this lane's query
 
   // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7].
-  bf16x8_t qf[C::DCH];  // loaded once the first tile's loads are in flight
+  opv8 qf[C::DCH];  // loaded once the first tile's loads are in flight
   const qelem* const qrow = static_cast<const qelem*>(p.q) +
                             (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
                             (int64_t)head * p.q_hs;
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
       const int chunk = stid + i * C::STAGERS;
       if (C::K_TOTAL % C::STAGERS == 0 || chunk < C::K_TOTAL)
         *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
-            kv_to_bf16(KVT(), kst[i]);
+            kv_to_op(OP(), KVT(), kst[i]);
     }
   };
   // V transposed into stage `st` with the key order of the S^T accumulator:
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
       const int pos = 16 * (kq >> 2) + 4 * (((qq & 1) << 1) | (qq >> 1));
       u32x4_t r[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = kv_to_bf16(KVT(), vst[u][i]);
+      for (int i = 0; i < 4; ++i) r[i] = kv_to_op(OP(), KVT(), vst[u][i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         // element j of keys (i, i+1) -> one dword (v_perm_b32)
@@ -293,11 +298,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 #pragma unroll
   for (int c = 0; c < C::DBLK; ++c) o[c] = (f32x16_t){};
   f32x16_t s[kKB];
-  bf16x8_t pf[kKT];
+  opv8 pf[kKT];
   float m_run = -INFINITY;  // running (lazy) max of raw scores
   float l_run = 0.f;        // this lane's share of the running sum
   const float cmul = p.score_mult;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Whether every key of the tile at kv0 is visible to every row of this wave.
   auto tile_full = [&](int kv0) {
@@ -314,9 +318,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     for (int c = 0; c < C::DCH; ++c) {
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+        const opv8 a = *reinterpret_cast<const opv8*>(
             ks + (32 * kb + col) * C::KSTR + 16 * c + 8 * half);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+        s[kb] = OP::mfma(a, qf[c], s[kb]);
       }
     }
   };
@@ -327,9 +331,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     for (int c = 0; c < C::DBLK; ++c) {
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+        const opv8 a = *reinterpret_cast<const opv8*>(
             vs + (32 * c + col) * C::VSTR + 16 * kt + 8 * half);
-        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
+        o[c] = OP::mfma(a, pf[kt], o[c]);
       }
     }
   };
@@ -343,31 +347,30 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     constexpr int NPV = C::NPV, N = C::NPV + C::NS;
     // operand i < NPV: V^T for P.V step i (kt-major over the output blocks);
     // i >= NPV: K for score step i - NPV (d-chunk-major over the key blocks)
-    auto operand = [&](int i) -> bf16x8_t {
+    auto operand = [&](int i) -> opv8 {
       if (i >= NPV) {
         const int c = (i - NPV) / kKB, kb = (i - NPV) % kKB;
-        return *reinterpret_cast<const bf16x8_t*>(ks + (32 * kb + col) * C::KSTR + 16 * c +
-                                                  8 * half);
+        return *reinterpret_cast<const opv8*>(ks + (32 * kb + col) * C::KSTR + 16 * c +
+                                              8 * half);
       }
       const int kt = i / C::DBLK, c = i % C::DBLK;
-      return *reinterpret_cast<const bf16x8_t*>(vs + (32 * c + col) * C::VSTR + 16 * kt +
-                                                8 * half);
+      return *reinterpret_cast<const opv8*>(vs + (32 * c + col) * C::VSTR + 16 * kt +
+                                            8 * half);
     };
     constexpr int kAhead = N < 8 ? N : 8;
-    bf16x8_t buf[kAhead];
+    opv8 buf[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) buf[i] = operand(i);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const bf16x8_t a = buf[i % kAhead];
+      const opv8 a = buf[i % kAhead];
       if (i + kAhead < N) buf[i % kAhead] = operand(i + kAhead);
       if (i >= NPV) {
         const int c = (i - NPV) / kKB, kb = (i - NPV) % kKB;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? (f32x16_t){} : s[kb],
-                                                        0, 0, 0);
+        s[kb] = OP::mfma(a, qf[c], c == 0 ? (f32x16_t){} : s[kb]);
       } else {
         const int kt = i / C::DBLK, c = i % C::DBLK;
-        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
+        o[c] = OP::mfma(a, pf[kt], o[c]);
       }
     }
     // pin the order: kAhead LDS reads, then (MFMA, LDS read) pairs, then the
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
-  // Mask (boundary tiles only), online softmax into the bf16 P operand, and
+  // Mask (boundary tiles only), online softmax into the P operand, and
   // the lazy rescale of O and l.
   auto softmax = [&](int kv0) {
     if (!tile_full(kv0)) {
@@ -424,14 +427,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
         const float p0 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e], cmul, neg_mc));
         const float p1 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e + 1], cmul, neg_mc));
         // The dot product takes the converted pair itself: bit-casting an
-        // element of `u` back to bf16x2 made hipcc (ROCm 7.2) feed the same
+        // element of `u` back to a pair made hipcc (ROCm 7.2) feed the same
         // register to every v_dot2c of the group.
-        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        const typename OP::v2 pb = OP::cvt2(p0, p1);
         u[e] = __builtin_bit_cast(uint32_t, pb);
-        // l accumulates the bf16-rounded p that the P.V product uses
-        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
+        // l accumulates the rounded p that the P.V product uses
+        l4[e] = OP::sum2(pb, l4[e]);
       }
-      pf[kt] = __builtin_bit_cast(bf16x8_t, u);
+      pf[kt] = __builtin_bit_cast(opv8, u);
     }
     l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
     if (any) {
@@ -446,12 +449,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   // V(0) in flight (group B).
   if (group == 0) {
     gload_k(kv_start);
-    load_q_operand<C::DCH>(qrow, half, qmul, qf);
+    load_q_op<C::DCH, OP>(qrow, half, qmul, qf);
     store_k(0);
     if (n_tiles > 1) gload_k(kv_start + kBN);
   } else {
     gload_v(kv_start);
-    load_q_operand<C::DCH>(qrow, half, qmul, qf);
+    load_q_op<C::DCH, OP>(qrow, half, qmul, qf);
   }
   __syncthreads();
 

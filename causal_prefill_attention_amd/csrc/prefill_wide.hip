@@ -66,6 +66,8 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   using C = WideCfg<DQK, DV>;
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
+  typedef typename OpOf<KVT>::T OP;  // operand type of both products
+  typedef typename OP::v8 opv8;
   constexpr int kStage = 2 * C::K_ELEMS + 2 * C::V_ELEMS;
   constexpr int kOut = kXWaves * 32 * (DV + 8);
   __shared__ __attribute__((aligned(16))) uint16_t smem[kStage > kOut ? kStage : kOut];
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   const int mypos = hist + myq;
 
   // ---- Qᵀ operand: lane holds q[myq, 16c + 8*half .. +7]
-  bf16x8_t qf[C::DCH];  // loaded once the first tile's loads are in flight
+  opv8 qf[C::DCH];  // loaded once the first tile's loads are in flight
   const qelem* const qrow = static_cast<const qelem*>(p.q) +
                             (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
                             (int64_t)head * p.q_hs;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
     for (int i = 0; i < C::K_CHUNKS; ++i) {
       const int chunk = tid + i * kXThreads;
       *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
-          kv_to_bf16(KVT(), kst[i]);
+          kv_to_op(OP(), KVT(), kst[i]);
     }
   };
   auto store_v = [&](int st) {
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
       const int pos = 16 * (kq >> 2) + 4 * (((qq & 1) << 1) | (qq >> 1));
       u32x4_t r[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = kv_to_bf16(KVT(), vst[u][i]);
+      for (int i = 0; i < 4; ++i) r[i] = kv_to_op(OP(), KVT(), vst[u][i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
@@ -193,11 +195,10 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
 #pragma unroll
   for (int c = 0; c < C::DBLK; ++c) o[c] = (f32x16_t){};
   f32x16_t s[kXKB];
-  bf16x8_t pf[kXKT];
+  opv8 pf[kXKT];
   float m_run = -INFINITY;
   float l_run = 0.f;
   const float cmul = p.score_mult;
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   auto tile_full = [&](int kv0) {
     return (kv0 + kXBN - 1 <= hist + wq0) &&
@@ -211,9 +212,9 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
     for (int c = 0; c < C::DCH; ++c)
 #pragma unroll
       for (int kb = 0; kb < kXKB; ++kb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+        const opv8 a = *reinterpret_cast<const opv8*>(
             ks + (32 * kb + col) * C::KSTR + 16 * c + 8 * half);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+        s[kb] = OP::mfma(a, qf[c], s[kb]);
       }
   };
   auto pv = [&](int st) {
@@ -222,9 +223,9 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
     for (int kt = 0; kt < kXKT; ++kt)
 #pragma unroll
       for (int c = 0; c < C::DBLK; ++c) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+        const opv8 a = *reinterpret_cast<const opv8*>(
             vs + (32 * c + col) * C::VSTR + 16 * kt + 8 * half);
-        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt], o[c], 0, 0, 0);
+        o[c] = OP::mfma(a, pf[kt], o[c]);
       }
   };
   auto softmax = [&](int kv0) {
@@ -260,11 +261,11 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
         const float p0 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e], cmul, neg_mc));
         const float p1 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e + 1], cmul, neg_mc));
         // (the converted pair feeds the dot product directly; see the 128-d kernel)
-        const bf16x2_t pb = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        const typename OP::v2 pb = OP::cvt2(p0, p1);
         u[e] = __builtin_bit_cast(uint32_t, pb);
-        l4[e] = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, l4[e], false);
+        l4[e] = OP::sum2(pb, l4[e]);
       }
-      pf[kt] = __builtin_bit_cast(bf16x8_t, u);
+      pf[kt] = __builtin_bit_cast(opv8, u);
     }
     l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
     if (any) {
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   // wave finished before the previous barrier.  One barrier per tile.
   gload_k(kv_start);
   gload_v(kv_start);
-  load_q_operand<C::DCH>(qrow, half, qmul, qf);
+  load_q_op<C::DCH, OP>(qrow, half, qmul, qf);
   store_k(0);
   store_v(0);
   __syncthreads();

@@ -31,9 +31,13 @@
  * Sequences are packed back to back along the token axis; sequence s owns
  * tokens [cu_seqlens[s], cu_seqlens[s+1]).
  *
- * Precision.  Q (bf16 or fp32) and K/V (bf16 or fp16) are rounded to bf16
- * (round to nearest even) when loaded; both contractions run on bf16 MFMA
- * with fp32 accumulation; softmax statistics are fp32; out is bf16 (RNE).
+ * Precision.  Both contractions run on the matrix cores in the K/V storage
+ * type with fp32 accumulation, so that K and V enter them exactly as stored
+ * (the pages' FP16 storage with FP32 compute): bf16 K/V use the bf16 MFMA,
+ * fp16 K/V the fp16 MFMA.  Q (bf16 or fp32) and the softmax probabilities
+ * are rounded to that type (round to nearest even) -- with fp16 K/V, q must
+ * lie within the fp16 range (|q| <= 65504); softmax statistics are fp32; out
+ * is bf16 (RNE).
  *
  * Ownership and ordering.  The caller owns every buffer; the library keeps
  * no pointer after the call returns and allocates nothing.  The call is

@@ -1044,20 +1044,66 @@ def test_head_dim_512_dtypes(qd, kvd):
     check(w.name, to64(out), oracle_of(inp, 4, 2, w.attn_scale, 0))
 
 
-@pytest.mark.xfail(strict=False, reason=(
-    "the 512-d kernel narrows fp32 q and fp16 k/v to bf16 before its products; "
-    "with x30 K outliers that rounding alone moves the exact result by up to "
-    "0.056 max / 0.0025 mean (measured with the oracle on bf16-rounded inputs), "
-    "past the 2e-2 / 2e-3 bar"))
 def test_head_dim_512_fp32_fp16_outliers():
     """fp32 q and fp16 k with x30 outliers against the exact oracle on the
-    inputs as stored."""
+    inputs as stored (the products run in fp16, K/V as stored)."""
     w = workloads.custom("d512_fp32_fp16_outliers", [200, 1, 77], 4, 2, head_dim=512,
                          q_dtype="fp32", kv_dtype="fp16", seed=132, k_outlier_frac=0.01)
     _announce(w.name)
     inp = workloads.make_inputs(w)
     out = run_gpu(inp, 4, 2, 512, w.attn_scale, 0)
     check(w.name, to64(out), oracle_of(inp, 4, 2, w.attn_scale, 0))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_fp16_kv_with_outliers_against_exact_oracle(d):
+    """fp32 q, fp16 k/v with 1% of the K entries x30, causal and windowed,
+    through the kernel of every head size: fp16 K/V run the fp16 products,
+    so the exact oracle on the stored inputs is the reference."""
+    w = workloads.custom(f"fp16kv_outliers_d{d}", [200, 1, 77, 300], 4, 2, head_dim=d,
+                         q_dtype="fp32", kv_dtype="fp16", seed=140 + d, k_outlier_frac=0.01)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    for window in (0, 50):
+        out = run_gpu(inp, 4, 2, d, w.attn_scale, window)
+        check(f"{w.name}_w{window}", to64(out), oracle_of(inp, 4, 2, w.attn_scale, window))
+
+
+def test_mla_absorbed_fp16_cache_with_outliers():
+    """The absorbed 320 / 256 MLA shape over an fp16 cache with x30 outliers
+    in 1% of the rope columns (256..319) of the cache rows.  v is the first
+    256 columns, so the outliers touch the keys only: outliers in v would
+    make outputs of magnitude ~100, whose bf16 rounding alone exceeds the
+    absolute bar."""
+    w = workloads.custom("mla_fp16_outliers", [150, 1, 260], 8, 1, head_dim=320,
+                         q_dtype="fp32", kv_dtype="fp16", seed=146,
+                         scale=1.0 / math.sqrt(320))
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    rope = inp["k"][:, :, 256:].to(torch.float64).contiguous()
+    rng = np.random.default_rng(1460)
+    idx = rng.choice(rope.numel(), size=rope.numel() // 100, replace=False)
+    flat = rope.reshape(-1)
+    flat[torch.from_numpy(idx)] *= 30.0
+    inp["k"] = torch.cat([inp["k"][:, :, :256], rope.to(torch.float16)], dim=2)
+    inp["v"] = inp["k"][:, :, :256]
+    inp["head_dim_v"] = 256
+    out = run_gpu(inp, 8, 1, 320, w.attn_scale, 0)
+    check(w.name, to64(out), oracle_of(inp, 8, 1, w.attn_scale, 0))
+
+
+def test_decode_fp16_kv_with_outliers():
+    w = workloads.custom("decode_fp16_outliers", [1] * 12, 8, 2, q_dtype="fp32",
+                         kv_dtype="fp16", seed=147, k_outlier_frac=0.01,
+                         history=[0, 1, 63, 64, 65, 500, 1000, 7, 2000, 129, 31, 300])
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    inp["decode"] = True
+    for window in (0, 40):
+        out = run_gpu(inp, 8, 2, 128, w.attn_scale, window)
+        want = oracle.attention_decode(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_k"], 8, 2,
+                                       w.attn_scale, window)
+        check(f"{w.name}_w{window}", to64(out), want)
 
 
 def test_head_dim_512_chunked_and_paged():
