@@ -18,6 +18,14 @@ untimed warm-up steps, then exactly K timed steps bracketed by
   same workload (a subset of the query heads, all tokens), scaled to the
   same unit, with the number of threads it used.
 
+After the timed region, from the same process and without touching
+``value``: the other problem shapes of the metric (128 tokens, 2048 tokens,
+the 4096-token window, the packed GQA batch) each timed on their own
+(``other_configs``), a sustained run of the main workload for a few seconds
+with the graphics clock read from sysfs while it runs (``sustained``), the
+ROCm and HIP versions (``env``), and the oracle on one core for the two
+smallest shapes (``cpu_baseline.single_core``).
+
 ``--mode copy`` instead runs a plain device-to-device copy of known size;
 its rocprofv3 FETCH_SIZE / WRITE_SIZE readings calibrate the counters.
 """
@@ -27,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -110,58 +119,24 @@ def cpu_baseline(w, inp, n_heads_sample: int):
     }
 
 
-def run_copy(args):
-    import torch
-
-    n = args.copy_mib * (1 << 20)
-    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(args.warmup):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
-    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n,
-                      "ms_per_copy": dt * 1e3, "GB/s": 2 * n / dt / 1e9}))
+#: The other problem shapes of the metric, reported beside the main line.
+OTHER_CONFIGS = ["causal_128tok_4q1kv", "mla_2048tok_32q1kv", "window1024_4096tok_32q1kv",
+                 "varlen16_gqa32q8kv_fp32q_fp16kv"]
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=None)
-    ap.add_argument("--cpu-heads", type=int, default=0,
-                    help="query heads of the workload the CPU oracle times "
-                         "(default: all of them)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["attn", "copy"], default="attn")
-    ap.add_argument("--copy-mib", type=int, default=1024)
-    args = ap.parse_args()
+def rocm_version():
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return None
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(prefill attention would shard by query head or by sequence "
-              "with no exchange); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
 
-    import torch
+def make_step(w, binding, dev, stream):
+    """Device inputs of workload ``w`` and a closure that runs one call."""
+    from causal_prefill_attention_amd import workloads
 
-    if args.mode == "copy":
-        run_copy(args)
-        return
-
-    from causal_prefill_attention_amd import binding, measure, workloads
-
-    name = args.workload or workloads.HEADLINE
-    w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
-    lengths = inp["lengths"]
-    dev = torch.device("cuda:0")
     q = inp["q"].to(dev)
     k = inp["k"].to(dev)
     v = inp["v"].to(dev)
@@ -171,8 +146,9 @@ def main():
     dv = w.head_dim_v or w.head_dim
     if w.head_dim_v is not None:
         v = k[:, :, :w.head_dim_v]  # the values are part of the cache rows
+    import torch
     out = torch.empty(q.shape[0], w.n_q_heads, dv, dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    lengths = inp["lengths"]
     # partial results of key ranges split across workgroups (decode batches
     # and prefill calls that would not fill the chip; allocated once, outside
     # the timed region)
@@ -206,6 +182,209 @@ def main():
                                          w.n_kv_heads, w.head_dim, w.attn_scale,
                                          w.window, stream=stream)
 
+    return inp, workspace, step
+
+
+def time_launches(step, stream, n, warmup):
+    """Per-launch durations (ms) from HIP events on the launch stream."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def other_configs(binding, dev, stream):
+    """Kernel time of the metric's other problem shapes, each on its own."""
+    from causal_prefill_attention_amd import measure, workloads
+
+    res = {}
+    for name in OTHER_CONFIGS:
+        w = workloads.WORKLOADS[name]
+        inp, _, step = make_step(w, binding, dev, stream)
+        n = 1000 if sum(inp["lengths"]) <= 128 else 50
+        durs = time_launches(step, stream, n, warmup=10)
+        med = statistics.median(durs)
+        flops = measure.causal_flops(inp["lengths"], w.n_q_heads, w.head_dim, w.window,
+                                     inp.get("kv_lengths"), w.head_dim_v)
+        tf = flops / (med * 1e-3) / 1e12
+        res[name] = {"kernel_median_us": round(med * 1e3, 2),
+                     "kernel_avg_us": round(sum(durs) / len(durs) * 1e3, 2),
+                     "kernel_min_us": round(min(durs) * 1e3, 2),
+                     "launches": n, "causal_flops": flops,
+                     "tflops_at_median": round(tf, 2),
+                     "pct_of_peak": round(100.0 * tf / measure.PEAK_BF16_TFLOPS, 2)}
+    return res
+
+
+def sclk_path(dev):
+    """The device's ``pp_dpm_sclk`` sysfs file (graphics clock levels, the
+    current one starred), found through its PCI address."""
+    import torch
+
+    props = torch.cuda.get_device_properties(dev)
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is None:
+        return None
+    dom = getattr(props, "pci_domain_id", 0) or 0
+    devid = getattr(props, "pci_device_id", 0) or 0
+    path = f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{devid:02x}.0/pp_dpm_sclk"
+    return path if os.path.exists(path) else None
+
+
+def read_sclk_mhz(path):
+    """Current graphics clock (MHz) from the starred ``pp_dpm_sclk`` line."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if "*" in line:
+                    num = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
+                    return int(num) if num else None
+    except OSError:
+        return None
+    return None
+
+
+def sustained_run(step, stream, seconds, dev):
+    """Runs ``step`` back to back for about ``seconds`` while a thread reads
+    the graphics clock from sysfs every 10 ms.  Returns the average launch
+    time over the last third of the run and the clock readings."""
+    import threading
+
+    import torch
+
+    path = sclk_path(dev)
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            mhz = read_sclk_mhz(path) if path else None
+            if mhz is not None:
+                samples.append((time.perf_counter(), mhz))
+            stop.wait(0.01)
+
+    batch = 50
+    marks = []  # (start event, end event) per batch
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(batch):
+            step()
+        b.record(stream)
+        marks.append((a, b))
+        if len(marks) >= 2:
+            marks[-2][1].synchronize()  # keep at most two batches queued
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    stop.set()
+    th.join()
+    per_batch = [x.elapsed_time(y) / batch for x, y in marks]
+    tail = per_batch[-max(1, len(per_batch) // 3):]
+    load = [mhz for t, mhz in samples if t0 + 0.1 <= t <= t_end]
+    last = [mhz for t, mhz in samples if t_end - (t_end - t0) / 3 <= t <= t_end]
+
+    def mean(x):
+        return round(sum(x) / len(x), 1) if x else None
+
+    return {"seconds": round(t_end - t0, 2), "launches": batch * len(marks),
+            "last_third_avg_us": round(1e3 * sum(tail) / len(tail), 2),
+            "first_batch_avg_us": round(1e3 * per_batch[0], 2),
+            "gpu_clock": {"source": path, "samples": len(load),
+                          "mhz_mean_under_load": mean(load),
+                          "mhz_mean_last_third": mean(last),
+                          "mhz_min": min(load) if load else None,
+                          "mhz_max": max(load) if load else None}}
+
+
+def cpu_single_core(names):
+    """The oracle on one thread for the smallest problem shapes (seconds)."""
+    import oracle
+    from causal_prefill_attention_amd import workloads
+
+    res = {}
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        inp = workloads.make_inputs(w)
+        t0 = time.perf_counter()
+        oracle.attention_varlen(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"],
+                                w.n_q_heads, w.n_kv_heads, w.attn_scale, w.window,
+                                workers=1)
+        res[name] = round(time.perf_counter() - t0, 3)
+    return res
+
+
+def run_copy(args):
+    import torch
+
+    n = args.copy_mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n,
+                      "ms_per_copy": dt * 1e3, "GB/s": 2 * n / dt / 1e9}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="query heads of the workload the CPU oracle times "
+                         "(default: all of them)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other shapes, the sustained run and the "
+                         "single-core oracle times")
+    ap.add_argument("--sustain-s", type=float, default=2.0)
+    ap.add_argument("--mode", choices=["attn", "copy"], default="attn")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(prefill attention would shard by query head or by sequence "
+              "with no exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.mode == "copy":
+        run_copy(args)
+        return
+
+    from causal_prefill_attention_amd import binding, measure, workloads
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    inp, workspace, step = make_step(w, binding, dev, stream)
+    lengths = inp["lengths"]
+    kv_lengths = inp.get("kv_lengths")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -221,7 +400,8 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
+    in_order = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
+    durs = sorted(in_order)
     avg_ms = sum(durs) / len(durs)
 
     flops = measure.causal_flops(lengths, w.n_q_heads, w.head_dim, w.window, kv_lengths,
@@ -278,13 +458,25 @@ def main():
             **roof,
             "traffic": traffic,
             "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "kernel_median_us": round(statistics.median(durs) * 1e3, 2),
             "kernel_min_us": round(durs[0] * 1e3, 2),
+            "kernel_us_in_order": [round(x * 1e3, 1) for x in in_order],
             "algorithmic_bytes": alg_bytes,
         },
         "cpu_baseline": None,
     }
+    line["env"] = {"rocm": rocm_version(), "hip_runtime": torch.version.hip,
+                   "torch": torch.__version__,
+                   "device": torch.cuda.get_device_name(dev),
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count}
+    if not args.no_extras:
+        line["sustained"] = sustained_run(step, stream, args.sustain_s, dev)
+        line["other_configs"] = other_configs(binding, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads or w.n_q_heads)
+        if not args.no_extras:
+            line["cpu_baseline"]["single_core"] = {
+                "seconds": cpu_single_core(OTHER_CONFIGS[:2]), "cores": 1, "kind": "oracle"}
     print(json.dumps(line), flush=True)
 
 
