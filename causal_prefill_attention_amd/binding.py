@@ -25,6 +25,7 @@ ATTN_FP32 = 2
 #: Every symbol include/attn_prefill.h declares.
 EXPORTS = ("attn_prefill", "attn_prefill_chunked", "attn_prefill_paged", "attn_prefill_ex",
            "attn_decode", "attn_decode_paged", "attn_decode_ws", "attn_decode_paged_ws",
+           "attn_decode_noalloc",
            "attn_decode_workspace_size", "attn_prefill_ex_ws", "attn_prefill_workspace_size",
            "attn_prefill_status_string",
            "attn_prefill_last_error", "attn_prefill_supported_head_dims",
@@ -118,6 +119,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_paged_ws.restype = ctypes.c_int
     lib.attn_decode_paged_ws.argtypes = lib.attn_decode_paged.argtypes[:-1] + [
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_decode_noalloc.restype = ctypes.c_int
+    lib.attn_decode_noalloc.argtypes = lib.attn_decode.argtypes
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_decode_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32,
                                                ctypes.c_int32, ctypes.c_int32]
@@ -289,6 +292,18 @@ def call_raw_decode_paged_ws(q: AttnTensor, k_pool: AttnTensor, v_pool: AttnTens
                                     ctypes.c_void_p(stream))
 
 
+def call_raw_decode_noalloc(q: AttnTensor, k: AttnTensor, v: AttnTensor, out: AttnTensor,
+                            seqlens_k: AttnSeqlens, n_q_heads: int, n_kv_heads: int,
+                            head_dim: int, scale: float, sliding_window: int,
+                            stream: Optional[int] = None) -> int:
+    """Calls ``attn_decode_noalloc`` with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_decode_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                   ctypes.byref(out), ctypes.byref(seqlens_k), int(n_q_heads),
+                                   int(n_kv_heads), int(head_dim), float(scale),
+                                   int(sliding_window), ctypes.c_void_p(stream))
+
+
 def decode_workspace_size(n_seqs: int, n_q_heads: int, n_kv_heads: int,
                           head_dim: int) -> int:
     """Bytes of workspace with which a decode batch uses its preferred split
@@ -437,6 +452,19 @@ def attn_decode(q, k, v, out, cu_seqlens_k, n_q_heads: int, n_kv_heads: int,
         status = call_raw_decode_ws(describe(q), describe(k), describe(v), describe(out), sk,
                                     n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
                                     ptr, nbytes, _stream_handle(q, stream))
+    if status != ATTN_OK:
+        raise AttnPrefillError(status, last_error())
+
+
+def attn_decode_noalloc(q, k, v, out, cu_seqlens_k, n_q_heads: int, n_kv_heads: int,
+                        head_dim: int, scale: float, sliding_window: int = 0,
+                        stream=None) -> None:
+    """``attn_decode`` that allocates nothing: a small batch splits its keys
+    through the library's static device scratch (``attn_decode_noalloc``)."""
+    sk = _seqlens(cu_seqlens_k, "cu_seqlens_k")
+    status = call_raw_decode_noalloc(describe(q), describe(k), describe(v), describe(out), sk,
+                                     n_q_heads, n_kv_heads, head_dim, scale, sliding_window,
+                                     _stream_handle(q, stream))
     if status != ATTN_OK:
         raise AttnPrefillError(status, last_error())
 

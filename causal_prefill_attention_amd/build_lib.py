@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["prefill_fwd.hip", "prefill_wide.hip", "prefill_d512.hip", "decode_fwd.hip",
-           "attn_prefill.cpp"]
+           "decode_scratch.hip", "attn_prefill.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

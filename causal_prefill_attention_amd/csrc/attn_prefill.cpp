@@ -772,6 +772,32 @@ size_t attn_decode_workspace_size(int64_t n_seqs, int32_t n_q_heads, int32_t n_k
   return (size_t)(units * n_splits * (int64_t)attnp::decode_partial_floats(head_dim) * 4);
 }
 
+int attn_decode_noalloc(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                        const attn_tensor* out, const attn_seqlens* cu_seqlens_k,
+                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                        int32_t sliding_window, attn_stream_t stream) {
+  g_last_error.clear();
+  if (cu_seqlens_k == nullptr) return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_k is NULL");
+  // the split attn_decode_ws makes with its preferred workspace (0: none);
+  // shapes outside the contract give 0 here and are rejected by run_decode
+  const size_t need = q != nullptr ? attn_decode_workspace_size(q->n_tokens, n_q_heads,
+                                                                n_kv_heads, head_dim)
+                                   : 0;
+  if (need > attnp::kDecodeScratchBytes)
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "this batch's key split needs %zu bytes of scratch, beyond the %zu bytes of "
+                "the static decode scratch; use attn_decode_ws with a workspace",
+                need, attnp::kDecodeScratchBytes);
+  void* ptr = nullptr;
+  if (need > 0) {
+    const hipError_t e = attnp::decode_static_scratch(&ptr);
+    if (e != hipSuccess)
+      return fail(ATTN_ERR_HIP, "static decode scratch lookup failed: %s", hipGetErrorString(e));
+  }
+  return run_decode(q, k, v, out, cu_seqlens_k, nullptr, n_q_heads, n_kv_heads, head_dim, scale,
+                    sliding_window, ptr, need, stream);
+}
+
 int attn_decode_paged(const attn_tensor* q, const attn_tensor* k_pool, const attn_tensor* v_pool,
                       const attn_tensor* out, const attn_paged_kv* paged, int32_t n_q_heads,
                       int32_t n_kv_heads, int32_t head_dim, float scale, int32_t sliding_window,

@@ -1,6 +1,7 @@
 // Internal interface between the C ABI host code and the HIP kernels.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -110,6 +111,14 @@ struct DecodeParams {
 constexpr int decode_partial_floats(int head_dim) { return 64 + 32 * head_dim; }
 // Most key ranges one decode unit is split into.
 constexpr int kMaxSplits = 64;
+
+// The decode split's static scratch (attn_decode_noalloc): room for 256
+// partial blocks of a 128-d unit, the most the preferred split of any batch
+// uses on a device of up to 256 compute units.
+constexpr size_t kDecodeScratchBytes = 256 * (size_t)decode_partial_floats(128) * 4;
+// Device address of the current device's static decode scratch (looked up
+// once per device).
+hipError_t decode_static_scratch(void** ptr);
 
 // Launches the decode kernel (head_dim 128, q bf16/fp32, kv bf16/fp16).
 hipError_t launch_decode(const DecodeParams& p, int head_dim, DType q_dtype, DType kv_dtype,

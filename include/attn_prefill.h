@@ -304,6 +304,27 @@ int attn_decode_paged_ws(const attn_tensor* q, const attn_tensor* k_pool,
 size_t attn_decode_workspace_size(int64_t n_seqs, int32_t n_q_heads,
                                   int32_t n_kv_heads, int32_t head_dim);
 
+/* Decode that allocates nothing, for callers that cannot call hipMalloc:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same operation, arguments and result as attn_decode_ws
+ * given attn_decode_workspace_size() bytes of workspace (the same split of
+ * the keys, bitwise the same output), with the split's partial results kept
+ * in a static device array of the library instead of a caller workspace:
+ * 4,259,840 bytes (256 partial blocks of 16,640 bytes), which every GPU the
+ * library runs on holds from the first split call on that device until the
+ * process ends.  A batch whose split would need more (only possible on a
+ * device of more than 256 compute units) is rejected with
+ * ATTN_ERR_UNSUPPORTED and a message naming both sizes; attn_decode_ws
+ * serves it.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (on different streams, or from different
+ * threads) race; calls on one stream are ordered.  Nothing in the array
+ * needs clearing between calls: each split call writes every partial it
+ * reads.  Other arguments, precision and errors as for attn_decode. */
+int attn_decode_noalloc(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                        const attn_tensor* out, const attn_seqlens* cu_seqlens_k,
+                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                        float scale, int32_t sliding_window, attn_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_prefill_status_string(int status);
 

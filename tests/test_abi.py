@@ -434,6 +434,37 @@ def test_decode_ws_paged_page_size_checked():
     assert rc == B.ATTN_ERR_UNSUPPORTED and "page_size 32" in B.last_error()
 
 
+def call_decode_noalloc(**kw):
+    return B.call_raw_decode_noalloc(kw["q"], kw["k"], kw["v"], kw["out"], kw["seqlens_k"],
+                                     kw["n_q_heads"], kw["n_kv_heads"], kw["head_dim"],
+                                     kw["scale"], kw["sliding_window"], None)
+
+
+@pytest.mark.parametrize("name,mut,status,frag", BAD_DECODE, ids=[b[0] for b in BAD_DECODE])
+def test_decode_noalloc_checks_the_same_arguments(name, mut, status, frag):
+    rc = call_decode_noalloc(**mut(decode_args()))
+    assert rc == status, (rc, B.last_error())
+    assert frag in B.last_error(), B.last_error()
+
+
+def test_decode_noalloc_null_offsets_and_empty_batch():
+    lib = B.load_library()
+    a = decode_args()
+    rc = lib.attn_decode_noalloc(ctypes.byref(a["q"]), ctypes.byref(a["k"]),
+                                 ctypes.byref(a["v"]), ctypes.byref(a["out"]), None, 32, 8,
+                                 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG and "cu_seqlens_k is NULL" in B.last_error()
+    rc = lib.attn_decode_noalloc(None, ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                                 ctypes.byref(a["out"]), ctypes.byref(a["seqlens_k"]), 32, 8,
+                                 128, 0.1, 0, None)
+    assert rc == B.ATTN_ERR_INVALID_ARG, B.last_error()
+    e = decode_args(n_seqs=0)
+    for key in ("q", "out"):
+        e[key] = mutate(e[key], data=None)
+    assert call_decode_noalloc(**e) == B.ATTN_OK
+    assert B.last_error() == ""
+
+
 @pytest.mark.parametrize("args", [(0, 32, 1, 128), (4, 32, 1, 64), (4, 30, 8, 128),
                                   (4, 0, 1, 128), (-1, 32, 1, 128),
                                   ((1 << 31), 32, 1, 128), ((1 << 63) - 1, 32, 8, 128)])
