@@ -125,6 +125,66 @@ __device__ __forceinline__ void load_q_op(const T* qp, int half, float mult,
   for (int c = 0; c < DCH; ++c) qf[c] = to_op8<OP>(f[c], mult);
 }
 
+// The Qᵀ MFMA operands of one wave's 32 query rows, loaded through the
+// wave's own LDS slice (32 rows of `pitch` elements).  Whole rows are read
+// with 16-byte loads, one lane per 16-byte chunk (RPI rows per
+// instruction), so that every load instruction touches a few whole cache
+// lines; each chunk is multiplied by its row's multiplier (mult, or 0 for a
+// row at or past nvalid), rounded to the operand type and written to the
+// slice; then lane (col, half) reads back its operand chunks of row col.
+// Row r of the wave is token tok0 + row0 + r of qhead (token stride q_ts
+// elements); a row at or past nvalid reads token tok0 instead (a real row,
+// blanked by its zero multiplier).  The caller must keep other writers off
+// the slice until every wave of the workgroup has read its operands.
+template <int HDIM, class OP, class T>
+__device__ __forceinline__ void load_q_op_lds(const T* qhead, int64_t q_ts, int tok0, int row0,
+                                              int nvalid, float mult, uint16_t* slice,
+                                              int pitch, int lane, typename OP::v8* qf) {
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = HDIM / EPC;           // chunks per row
+  static_assert(CPR <= 64 && 64 % CPR == 0, "a load instruction covers whole rows");
+  constexpr int RPI = 64 / CPR;             // rows per load instruction
+  constexpr int NI = 32 / RPI;              // load instructions per wave
+  const int rr = lane / CPR, ch = lane % CPR;
+  u32x4_t raw[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = RPI * i + rr;
+    const int tok = tok0 + (r < nvalid ? row0 + r : 0);
+    raw[i] = load16(qhead + (int64_t)tok * q_ts + EPC * ch);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = RPI * i + rr;
+    const float m = r < nvalid ? mult : 0.f;
+    uint16_t* dst = slice + r * pitch + EPC * ch;
+    if constexpr (EPC == 8) {  // 16-bit elements (bf16)
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(raw[i][e] << 16);
+        f[2 * e + 1] = __uint_as_float(raw[i][e] & 0xffff0000u);
+      }
+      *reinterpret_cast<typename OP::v8*>(dst) = to_op8<OP>(f, m);
+    } else {  // fp32
+      u32x2_t u;
+      u[0] = __builtin_bit_cast(uint32_t, OP::cvt2(__uint_as_float(raw[i][0]) * m,
+                                                   __uint_as_float(raw[i][1]) * m));
+      u[1] = __builtin_bit_cast(uint32_t, OP::cvt2(__uint_as_float(raw[i][2]) * m,
+                                                   __uint_as_float(raw[i][3]) * m));
+      *reinterpret_cast<u32x2_t*>(dst) = u;
+    }
+  }
+  // the slice is the wave's own: LDS operations of one wave complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < HDIM / 16; ++c)
+    qf[c] = *reinterpret_cast<const typename OP::v8*>(slice + col * pitch + 16 * c + 8 * half);
+}
+
 // Value of the other half-wave's lane (l <-> l ^ 32) combined with ours.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),

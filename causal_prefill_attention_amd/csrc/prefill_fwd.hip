@@ -188,12 +188,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int myq = wq0 + col;
   const int mypos = hist + myq;  // key position of this lane's query
 
-  // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7].
-  opv8 qf[C::DCH];  // loaded once the first tile's loads are in flight
-  const qelem* const qrow = static_cast<const qelem*>(p.q) +
-                            (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
-                            (int64_t)head * p.q_hs;
-  const float qmul = myq < w.len ? p.q_mult : 0.f;
+  // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7], loaded once the
+  // first tile's loads are in flight, through the wave's LDS slice (the
+  // epilogue's), with whole-row loads.
+  opv8 qf[C::DCH];
+  const qelem* const qhead = static_cast<const qelem*>(p.q) + (int64_t)head * p.q_hs;
+  constexpr int QSTR = HDIM + 8;  // Q / O slice row pitch in LDS (16-bit elements)
+  static_assert(kWaves * 32 * QSTR <= 2 * C::K_ELEMS + 2 * C::V_ELEMS, "Q slices fit");
+  auto load_q = [&]() {
+    load_q_op_lds<HDIM, OP>(qhead, p.q_ts, w.start, wq0, w.len - wq0, p.q_mult,
+                            smem + wave * 32 * QSTR, QSTR, lane, qf);
+  };
 
   // ---- K/V tile movement (K by group A, V by group B).  Per-sequence bases
   // are wave-uniform; each tile is read through a buffer resource covering
@@ -446,15 +451,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   };
 
   // ---- prologue: K(0) stored in stage 0 and K(1) in flight (group A),
-  // V(0) in flight (group B).
+  // V(0) in flight (group B).  K stage 0 overlaps Q slices, so it is
+  // written only once every wave holds its Q operand.
   if (group == 0) {
     gload_k(kv_start);
-    load_q_op<C::DCH, OP>(qrow, half, qmul, qf);
+    load_q();
+    __syncthreads();
     store_k(0);
     if (n_tiles > 1) gload_k(kv_start + kBN);
   } else {
     gload_v(kv_start);
-    load_q_op<C::DCH, OP>(qrow, half, qmul, qf);
+    load_q();
+    __syncthreads();
   }
   __syncthreads();
 
@@ -542,8 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   // 32 x HDIM tile goes through its own LDS slice (free after the last
   // barrier) so that every global store writes whole 2*HDIM-byte rows.
   if (wave_live) {
-    constexpr int OSTR = HDIM + 8;  // row pitch in LDS (bf16 elements)
-    static_assert(kWaves * 32 * OSTR <= 2 * C::K_ELEMS + 2 * C::V_ELEMS, "O slices fit");
+    constexpr int OSTR = QSTR;
     uint16_t* ob = smem + wave * 32 * OSTR;
     // rows past the sequence are never stored; a row without any visible
     // key (malformed offsets only) is written as zeros
