@@ -131,10 +131,17 @@ __device__ __forceinline__ KeyRange key_range(const PrefillParams& p, const Work
 // heads: wave w runs head 4 * group_index + w % 4 on rows 32 * (w / 4) ..
 // +31 of the tile, so every K/V tile staged in LDS serves four heads and a
 // query tile's causal diagonal spans one key tile instead of four.
-template <int HDIM, class QT, class KVT, bool PAGED, bool SPLIT, int HP>
+// FOLD (HP = 4, causal without a window): group A runs the 32-row block r
+// of the sequence and group B its mirror nb - 1 - r, so a workgroup's work
+// no longer grows with its position in the sequence.  Both see key tiles
+// from 0; group B, the later block, sees at least as many, and group A
+// stops its matrix and softmax work after its own last key tile (it keeps
+// staging K and passing the barriers), leaving the SIMDs to group B.
+template <int HDIM, class QT, class KVT, bool PAGED, bool SPLIT, int HP, bool FOLD>
 __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams p) {
   static_assert(HP == 1 || (HP == 4 && !SPLIT), "head packing is for unsplit tiles");
-  constexpr int BMQ = kBM / HP;  // query rows per head
+  static_assert(!FOLD || HP == 4, "folded grids pack four heads");
+  constexpr int BMQ = FOLD ? 32 : kBM / HP;  // query rows per head (per group when folded)
   using C = Cfg<HDIM>;
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
@@ -155,17 +162,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int head = hbase + (HP == 1 ? 0 : (wave & (HP - 1)));  // wave-uniform
   const int slot = SPLIT ? unit / p.max_pieces : unit;
   const int piece = SPLIT ? unit - slot * p.max_pieces : 0;
-  Work w = decode_work<BMQ, PAGED>(p, slot);
+  Work w = decode_work<BMQ, PAGED, FOLD>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
   w.start = __builtin_amdgcn_readfirstlane(w.start);
   w.len = __builtin_amdgcn_readfirstlane(w.len);
   w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
+  w.q0_b = __builtin_amdgcn_readfirstlane(w.q0_b);
   w.kstart = __builtin_amdgcn_readfirstlane(w.kstart);
   w.seq = __builtin_amdgcn_readfirstlane(w.seq);
   w.klen = __builtin_amdgcn_readfirstlane(w.klen);
 
   const int kvh = hbase / p.group;  // the same for every head of the workgroup
-  const KeyRange kr = key_range<BMQ>(p, w);
+  // Folded: the key range is group B's (the mirror block, kv_start 0); group
+  // A's tiles are its first n_a (none when the two blocks coincide).
+  Work wb = w;
+  wb.q0 = w.q0_b;
+  const KeyRange kr = key_range<BMQ>(p, wb);
+  const bool a_live = !FOLD || w.q0 != w.q0_b;
+  const int n_a = FOLD ? (a_live ? key_range<BMQ>(p, w).n_tiles : 0) : kr.n_tiles;
   const int hist = kr.hist;
   const int kv_hi = kr.kv_hi;
   int kv_start = kr.kv_start;
@@ -182,7 +196,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
 
   const int col = lane & 31;   // query column of this lane
   const int half = lane >> 5;  // which 8-wide half of each 16-wide k-step
-  const int wq0 = w.q0 + (HP == 1 ? wave : wave / HP) * 32;  // first row of this wave
+  // first row of this wave (a folded idle group A gets rows past the sequence)
+  const int wq0 = FOLD ? (group == 0 ? (a_live ? w.q0 : w.len) : w.q0_b)
+                       : w.q0 + (HP == 1 ? wave : wave / HP) * 32;
   const int wq_last = min(wq0 + 31, w.len - 1);
   const bool wave_live = wq0 < w.len;
   const int myq = wq0 + col;
@@ -479,27 +495,46 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   // prologue.  Every wave runs every tile: a tile none of its rows can see
   // is fully masked and contributes exact zeros.
   if (group == 0) {
-    // prologue (before the loop): K(0) stored, K(1) in flight
-    scores(0);
-    __syncthreads();
-    softmax(kv_start);
-    if (n_tiles > 1) {
-      store_k(1);
-      if (n_tiles > 2) gload_k(kv_start + 2 * kBN);
-    }
-    __syncthreads();
-    for (int j = 1; j < n_tiles; ++j) {
-      const int kv0 = kv_start + j * kBN;
-      matrix_fused(j & 1, (j - 1) & 1);
-      __syncthreads();
-      softmax(kv0);
+    // Group A computes tiles [0, n_a) (n_a = n_tiles unless folded) and
+    // stages K for all n_tiles: K(j + 1) stored and K(j + 2) issued in
+    // the slot after tile j's matrix slot.
+    auto stage_after = [&](int j) {
       if (j + 1 < n_tiles) {
         store_k((j + 1) & 1);
-        if (j + 2 < n_tiles) gload_k(kv0 + 2 * kBN);
+        if (j + 2 < n_tiles) gload_k(kv_start + (j + 2) * kBN);
       }
+    };
+    // prologue (before the loop): K(0) stored, K(1) in flight
+    if (!FOLD || n_a > 0) scores(0);
+    __syncthreads();
+    if (!FOLD || n_a > 0) softmax(kv_start);
+    stage_after(0);
+    __syncthreads();
+    const int n_full = FOLD ? max(n_a, 1) : n_tiles;
+    for (int j = 1; j < n_full; ++j) {
+      matrix_fused(j & 1, (j - 1) & 1);
+      __syncthreads();
+      softmax(kv_start + j * kBN);
+      stage_after(j);
       __syncthreads();
     }
-    pv((n_tiles - 1) & 1);
+    if (FOLD) {
+      // Folded: A's last P.V in tile n_a's matrix slot, then K staging only.
+      int j = n_full;
+      if (n_a > 0 && n_a < n_tiles) {
+        pv((n_a - 1) & 1);
+        __syncthreads();
+        stage_after(n_a);
+        __syncthreads();
+        j = n_a + 1;
+      }
+      for (; j < n_tiles; ++j) {
+        __syncthreads();
+        stage_after(j);
+        __syncthreads();
+      }
+    }
+    if (!FOLD || n_a == n_tiles) pv((n_tiles - 1) & 1);
     __syncthreads();
     __syncthreads();
   } else {
@@ -642,25 +677,31 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
 template <int HDIM, class QT, class KVT, bool PAGED>
 void launch_paged_or_not(PrefillParams p, uint64_t slots, hipStream_t stream) {
   if (p.piece_tiles == 0 && p.group % 4 == 0) {
-    // four heads of one KV head per workgroup, 64 rows each
+    // four heads of one KV head per workgroup, 64 rows each (or, folded,
+    // two mirrored 32-row blocks: ceil(ceil(n / 32) / 2) = ceil(n / 64)
+    // pairs for n tokens, the same slot count)
     constexpr int bm = kBM / 4;
     const uint64_t slots4 = (uint64_t)((p.n_tokens + bm - 1) / bm + p.n_seqs);
     p.tile_slots = (int32_t)slots4;
-    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 4>),
-                       dim3((uint32_t)(slots4 * (uint64_t)(p.n_q_heads / 4))), dim3(kThreads), 0,
-                       stream, p);
+    const dim3 grid((uint32_t)(slots4 * (uint64_t)(p.n_q_heads / 4)));
+    if (p.fold && p.window == 0)
+      hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 4, true>), grid,
+                         dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 4, false>), grid,
+                         dim3(kThreads), 0, stream, p);
     return;
   }
   if (p.piece_tiles > 0) {
     const uint64_t blocks = slots * (uint64_t)p.max_pieces * (uint64_t)p.n_q_heads;
-    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, true, 1>),
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, true, 1, false>),
                        dim3((uint32_t)blocks), dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL((prefill_merge_kernel<HDIM, PAGED>),
                        dim3((uint32_t)(slots * (uint64_t)p.n_q_heads *
                                        (uint64_t)(kBM / merge_rows<HDIM>()))),
                        dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 1>),
+    hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 1, false>),
                        dim3((uint32_t)(slots * (uint64_t)p.n_q_heads)), dim3(kThreads), 0,
                        stream, p);
   }

@@ -48,6 +48,12 @@ struct PrefillParams {
   int32_t piece_tiles = 0;    // 0 = every query tile in one workgroup
   int32_t max_pieces = 1;     // grid pieces per query-tile slot
   float* partial = nullptr;   // [slot][piece][head] blocks of prefill_partial_floats
+  // Folded grid (64-d and 128-d, four query heads per workgroup, causal
+  // without a window, no key split): a workgroup's two wave groups take the
+  // 32-row query blocks r and nb - 1 - r of one sequence instead of two
+  // adjacent ones, which evens out the causal work of a grid of about one
+  // workgroup per CU.
+  int32_t fold = 0;
 };
 
 // fp32 values of one partial block: running max and sum of each of bm rows,

@@ -20,6 +20,7 @@ struct Work {
   int q0;      // first local query row of this tile
   int seq;     // sequence index (the block-table row of a paged cache)
   bool valid;
+  int q0_b;    // folded grids: first local row of the second (mirrored) block
 };
 
 // Maps a q-tile slot to (sequence, tile).  Slots enumerate sequences in
@@ -27,7 +28,12 @@ struct Work {
 // first.  Query and key offsets are clamped into [0, T].  Every lane of the
 // wave computes the same answer.  With a paged cache the key count comes
 // from seqlens_k, clamped to the table row's capacity.
-template <int BM, bool PAGED>
+// FOLD: a slot is a pair of BM-row blocks of one sequence, block r and its
+// mirror nb - 1 - r (nb blocks in the sequence), so that every pair sees
+// about the same number of causal keys; rank 0 (the first block with the
+// last, the heaviest pair) comes first.  q0 is block r, q0_b the mirror;
+// they coincide for the middle block of an odd nb.
+template <int BM, bool PAGED, bool FOLD = false>
 __device__ Work decode_work(const PrefillParams& p, int slot) {
   const int lane = threadIdx.x & (kWorkWave - 1);
   int base = 0;
@@ -47,7 +53,8 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
     }
     if (s >= p.n_seqs) a = b = ka = kb = 0;
     const int len = max(b - a, 0);
-    const int nt = (len + BM - 1) / BM;
+    const int nb = (len + BM - 1) / BM;  // BM-row blocks
+    const int nt = FOLD ? (nb + 1) / 2 : nb;
     int incl = nt;
 #pragma unroll
     for (int off = 1; off < kWorkWave; off <<= 1) {
@@ -65,15 +72,21 @@ __device__ Work decode_work(const PrefillParams& p, int slot) {
       w.kstart = __shfl(ka, src, kWorkWave);
       w.klen = __shfl(max(kb - ka, 0), src, kWorkWave);
       const int ntiles = __shfl(nt, src, kWorkWave);
-      const int rank = slot - base - excl;  // 0 = heaviest tile
-      w.q0 = (ntiles - 1 - rank) * BM;
+      const int rank = slot - base - excl;  // 0 = heaviest tile (or pair)
+      if (FOLD) {
+        w.q0 = rank * BM;
+        w.q0_b = (__shfl(nb, src, kWorkWave) - 1 - rank) * BM;
+      } else {
+        w.q0 = (ntiles - 1 - rank) * BM;
+        w.q0_b = w.q0;
+      }
       w.seq = s0 + src;
       w.valid = true;
       return w;
     }
     base += total;
   }
-  Work w{0, 0, 0, 0, 0, 0, false};
+  Work w{0, 0, 0, 0, 0, 0, false, 0};
   return w;
 }
 

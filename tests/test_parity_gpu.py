@@ -272,6 +272,69 @@ def test_deterministic_bitwise():
     assert torch.equal(a, b)
 
 
+# Folded grids: a workgroup's two wave groups take 32-row query blocks r and
+# nb - 1 - r of a sequence.  Every row still meets key tiles 0, 1, ... in
+# order (the folded lighter block only drops trailing tiles it cannot see,
+# which add exact zeros), so folded and unfolded outputs agree bit for bit.
+FOLD_SHAPES = [([1], 4, 1), ([31], 4, 1), ([33], 8, 2), ([96], 4, 1), ([100], 32, 1),
+               ([257], 8, 2), ([1000], 4, 1), ([2048], 32, 1),
+               ([300, 64, 1, 191, 0, 33], 8, 2), ([65, 2, 129, 500], 16, 4)]
+
+
+def _fold_pair(monkeypatch, run):
+    monkeypatch.setenv("ATTN_PREFILL_FOLD", "1")
+    folded = run().clone()
+    monkeypatch.setenv("ATTN_PREFILL_FOLD", "0")
+    plain = run().clone()
+    monkeypatch.delenv("ATTN_PREFILL_FOLD")
+    return folded, plain
+
+
+@pytest.mark.parametrize("lengths,hq,hkv", FOLD_SHAPES)
+def test_folded_grid_matches_oracle_and_unfolded_bitwise(lengths, hq, hkv, monkeypatch):
+    name = f"fold_{'_'.join(map(str, lengths))}_h{hq}x{hkv}"
+    w = workloads.custom(name, lengths, hq, hkv, seed=64 + len(lengths) + hq)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    folded, plain = _fold_pair(monkeypatch,
+                               lambda: run_gpu(inp, hq, hkv, 128, w.attn_scale, 0))
+    check(name, to64(folded), oracle_of(inp, hq, hkv, w.attn_scale, 0))
+    assert torch.equal(folded, plain)
+
+
+@pytest.mark.parametrize("variant", ["chunked", "paged", "d64", "fp32q_fp16kv", "scale_neg"])
+def test_folded_grid_variants(variant, monkeypatch):
+    """Folding with a KV history, a paged cache, 64-d heads, fp32 Q with fp16
+    K/V, and a negative scale."""
+    hq, hkv, d, scale = 8, 2, 128, None
+    kw = {}
+    lengths = [190, 33, 400, 1]
+    if variant in ("chunked", "paged"):
+        kw["history"] = [500, 0, 129, 64]
+    if variant == "d64":
+        d = 64
+        kw["head_dim"] = 64
+    if variant == "fp32q_fp16kv":
+        kw.update(q_dtype="fp32", kv_dtype="fp16")
+    if variant == "scale_neg":
+        scale = -0.3
+    w = workloads.custom(f"fold_{variant}", lengths, hq, hkv, seed=65, scale=scale, **kw)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    if variant == "paged":
+        k_pool, v_pool, table = to_paged(inp, 128, seed=9)
+        folded, plain = _fold_pair(monkeypatch, lambda: run_paged(
+            inp, k_pool, v_pool, table, 128, hq, hkv, w.attn_scale, 0))
+        want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
+                                      inp["kv_lengths"], 128, hq, hkv, w.attn_scale, 0)
+    else:
+        folded, plain = _fold_pair(monkeypatch,
+                                   lambda: run_gpu(inp, hq, hkv, d, w.attn_scale, 0))
+        want = oracle_of(inp, hq, hkv, w.attn_scale, 0)
+    check(w.name, to64(folded), want)
+    assert torch.equal(folded, plain)
+
+
 @pytest.mark.parametrize("window", [0, 70])
 def test_head_packing_matches_single_heads_bitwise(window):
     """Four query heads of one KV head run in one workgroup (64 rows each);
