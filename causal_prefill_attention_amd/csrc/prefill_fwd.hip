@@ -36,9 +36,14 @@
 //   * The S^T accumulator, rounded to the operand type, is directly the B operand of
 //     O^T += V^T P^T.  The key order inside each 16-key MFMA step follows the
 //     accumulator layout; V^T is written into LDS in that permuted order.
-//   * The running max moves lazily: O and l are rescaled only when a query's
-//     max grows by more than 2^kLazy (a rare wave-uniform branch); l sums the
-//     rounded probabilities with v_dot2 so it matches what P.V uses.
+//   * The running max moves lazily and is not taken on the common tile: the
+//     probabilities are formed against the running reference m_run, and
+//     only when a lane's sum of them exceeds a cap (2^32 for bf16 operands,
+//     2^15 for fp16 ones, so that every probability stays in the operand's
+//     range), or on a row's first visible tile, does the wave take the
+//     tile's max, move m_run to it, rescale O and l and form the
+//     probabilities again (a rare wave-uniform branch).  l sums the rounded
+//     probabilities with v_dot2 so it matches what P.V uses.
 //   * Masks are applied only to tiles that straddle the diagonal or the
 //     window edge.  Every wave runs every tile of its workgroup; a tile none
 //     of its rows can see is fully masked and adds exact zeros.
@@ -75,8 +80,13 @@ constexpr int kBN = 64;        // keys per KV tile: two 32-key MFMA blocks
 constexpr int kKB = kBN / 32;
 constexpr int kKT = kBN / 16;  // 16-key MFMA k-steps of the P.V contraction
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-// Lazy-max threshold (log2 units): p = 2^(t - m) may reach 2^kLazy before m moves.
-constexpr float kLazy = 8.0f;
+// A lane's sum of one tile's probabilities (32 keys) relative to the running
+// reference m_run may reach this before m_run moves to the running max, so
+// that no probability exceeds it: 2^15 keeps fp16 operands in range; bf16
+// operands (the fp32 exponent range) and the fp32 sums and accumulators
+// keep full relative precision far beyond 2^32.
+template <class OP> constexpr float sum_cap() { return 4294967296.0f; }
+template <> constexpr float sum_cap<OpFP16>() { return 32768.0f; }
 
 template <int HDIM>
 struct Cfg {
@@ -406,39 +416,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   };
   // Mask (boundary tiles only), online softmax into the P operand, and
   // the lazy rescale of O and l.
-  auto softmax = [&](int kv0) {
-    if (!tile_full(kv0)) {
-      // Element r of key block kb holds key kv0 + 4*half + off, with the
-      // compile-time offset off = 32*kb + 8*(r/4) + r%4.  The key is visible
-      // when off <= hi (causal) and, with a window, off >= lo.
-      const int hi = mypos - kv0 - 4 * half;
-      // (lo <= 0 bounds nothing since off >= 0: the subtraction only runs where it
-      // cannot overflow; no branch, the same code with and without a window)
-      const int lo = (p.window > 0 && p.window <= hi) ? hi - p.window + 1 : INT_MIN;
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-          if (off > hi || off < lo) s[kb][r] = -INFINITY;
-        }
-    }
-    // Row max and row sum use four independent partial chains each: with one
-    // vector-ALU wave per SIMD in this slot, a single 32-long dependency
-    // chain would leave the ALU waiting on latency.
-    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = pair_max(mx);
-    const bool raise = (mx - m_run) * cmul > kLazy;  // true when m_run = -inf < mx
-    const bool any = __ballot(raise) != 0ull;        // wave-uniform
-    const float m_new = any ? fmaxf(m_run, mx) : m_run;
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
-    const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
-    m_run = m_new;
+  // Converts the tile's probabilities relative to neg_mc into the P operand
+  // and returns this lane's sum of the rounded values.
+  auto exp_tile = [&](float neg_mc) {
     float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
@@ -457,13 +437,54 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
       }
       pf[kt] = __builtin_bit_cast(opv8, u);
     }
-    l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
-    if (any) {
+    return (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  };
+  // Mask (boundary tiles only), online softmax into the P operand, and
+  // the lazy rescale of O and l.  The probabilities are first taken
+  // against the running reference m_run with no max pass; only when a
+  // lane's sum of them exceeds kSumCap (so one may exceed the operand's
+  // range), or on a row's first visible tile (m_run = -inf), does the wave
+  // take the tile's max and move m_run to it.
+  auto softmax = [&](int kv0) {
+    if (!tile_full(kv0)) {
+      // Element r of key block kb holds key kv0 + 4*half + off, with the
+      // compile-time offset off = 32*kb + 8*(r/4) + r%4.  The key is visible
+      // when off <= hi (causal) and, with a window, off >= lo.
+      const int hi = mypos - kv0 - 4 * half;
+      // (lo <= 0 bounds nothing since off >= 0: the subtraction only runs where it
+      // cannot overflow; no branch, the same code with and without a window)
+      const int lo = (p.window > 0 && p.window <= hi) ? hi - p.window + 1 : INT_MIN;
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off > hi || off < lo) s[kb][r] = -INFINITY;
+        }
+    }
+    float lt = exp_tile(m_run == -INFINITY ? 0.f : -m_run * cmul);
+    // (a NaN sum fails the comparison and takes the slow path too)
+    const bool raise = !(lt <= sum_cap<OP>()) || m_run == -INFINITY;
+    if (__ballot(raise) != 0ull) {  // wave-uniform, rare
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+      const float mx = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY || m_run == -INFINITY)
+                              ? (m_new == -INFINITY ? 1.f : 0.f)
+                              : fast_exp2((m_run - m_new) * cmul);
+      lt = exp_tile(m_new == -INFINITY ? 0.f : -m_new * cmul);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int c = 0; c < C::DBLK; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
     }
+    l_run += lt;
   };
 
   // ---- prologue: K(0) stored in stage 0 and K(1) in flight (group A),
