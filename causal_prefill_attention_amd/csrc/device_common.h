@@ -185,6 +185,73 @@ __device__ __forceinline__ void load_q_op_lds(const T* qhead, int64_t q_ts, int 
     qf[c] = *reinterpret_cast<const typename OP::v8*>(slice + col * pitch + 16 * c + 8 * half);
 }
 
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float pair_max(float x);
+
+// Lazy online softmax.  A lane's sum of one tile's probabilities against the
+// running reference m_run may reach this cap before m_run moves to the
+// running max, so no probability exceeds it: 2^15 keeps fp16 operands in
+// range; bf16 operands (the fp32 exponent range) and the fp32 sums and
+// accumulators keep full relative precision far beyond 2^32.
+template <class OP> constexpr float lazy_sum_cap() { return 4294967296.0f; }
+template <> constexpr float lazy_sum_cap<OpFP16>() { return 32768.0f; }
+
+// One tile of the online softmax in base 2 (scores in raw units times cmul =
+// |scale| log2 e).  The lane holds 8 * NKT masked scores, score(kt, i) for
+// MFMA k-step kt and i < 8, and fills the P operand pf[kt] with their
+// probabilities rounded to the operand type.  Common case: the
+// probabilities are taken against the running reference m_run with no max
+// pass.  When a lane's sum of them exceeds the cap, or on a row's first
+// visible tile (m_run = -inf), the wave (uniformly) takes the tile's max
+// over both half-waves, moves m_run to the running max, calls rescale(alpha)
+// for the caller's O accumulators and forms the probabilities again.  l_run
+// accumulates the rounded probabilities (v_dot2), the values the P.V
+// product uses.
+template <class OP, int NKT, class ScoreAt, class Rescale>
+__device__ __forceinline__ void lazy_softmax(const ScoreAt& score, float cmul, float& m_run,
+                                             float& l_run, typename OP::v8* pf,
+                                             const Rescale& rescale) {
+  auto exp_tile = [&](float neg_mc) {
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      u32x4_t u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(fmaf(score(kt, 2 * e), cmul, neg_mc));
+        const float p1 = fast_exp2(fmaf(score(kt, 2 * e + 1), cmul, neg_mc));
+        // The dot product takes the converted pair itself: bit-casting an
+        // element of `u` back to a pair made hipcc (ROCm 7.2) feed the same
+        // register to every v_dot2c of the group.
+        const typename OP::v2 pb = OP::cvt2(p0, p1);
+        u[e] = __builtin_bit_cast(uint32_t, pb);
+        l4[e] = OP::sum2(pb, l4[e]);
+      }
+      pf[kt] = __builtin_bit_cast(typename OP::v8, u);
+    }
+    return (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  };
+  float lt = exp_tile(m_run == -INFINITY ? 0.f : -m_run * cmul);
+  // (a NaN sum fails the comparison and takes the slow path too)
+  const bool raise = !(lt <= lazy_sum_cap<OP>()) || m_run == -INFINITY;
+  if (__ballot(raise) != 0ull) {  // wave-uniform, rare
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m4[i & 3] = fmaxf(m4[i & 3], score(kt, i));
+    const float mx = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+    const float m_new = fmaxf(m_run, mx);
+    // O and l are still zero while m_run = -inf
+    const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * cmul);
+    lt = exp_tile(m_new == -INFINITY ? 0.f : -m_new * cmul);
+    m_run = m_new;
+    l_run *= alpha;
+    rescale(alpha);
+  }
+  l_run += lt;
+}
+
 // Value of the other half-wave's lane (l <-> l ^ 32) combined with ours.
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -196,8 +263,6 @@ __device__ __forceinline__ float pair_sum(float x) {
                                                   false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace dev
 }  // namespace attnp

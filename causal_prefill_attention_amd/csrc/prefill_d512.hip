@@ -54,7 +54,6 @@ constexpr int kGSlice = 512 / kGSlices;     // 128 columns per slice
 constexpr int kGBM = 64;                    // query rows per workgroup (32 per group)
 constexpr int kGBN = 32;                    // keys per tile: one 32-key score block
 constexpr int kGKQ = kGBN / 16;             // 16-key P.V steps per tile
-constexpr float kGLazy = 8.0f;              // lazy-max threshold, log2 units
 
 template <class QT, class KVT, bool PAGED>
 __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParams p) {
@@ -230,39 +229,13 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
         if (off > hi || off < lo) sc[r] = -INFINITY;
       }
     }
-    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    lazy_softmax<OP, kGKQ>(
+        [&](int kt, int i) { return sc[8 * kt + i]; }, cmul, m_run, l_run, pf, [&](float alpha) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], sc[r]);
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = pair_max(mx);
-    const bool raise = (mx - m_run) * cmul > kGLazy;
-    const bool any = __ballot(raise) != 0ull;
-    const float m_new = any ? fmaxf(m_run, mx) : m_run;
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * cmul);
-    const float neg_mc = (m_new == -INFINITY) ? 0.f : -m_new * cmul;
-    m_run = m_new;
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < DBLK; ++c)
 #pragma unroll
-    for (int kq = 0; kq < kGKQ; ++kq) {
-      u32x4_t u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(sc[8 * kq + 2 * e], cmul, neg_mc));
-        const float p1 = fast_exp2(fmaf(sc[8 * kq + 2 * e + 1], cmul, neg_mc));
-        // (the converted pair feeds the dot product directly; see the 128-d kernel)
-        const typename OP::v2 pb = OP::cvt2(p0, p1);
-        u[e] = __builtin_bit_cast(uint32_t, pb);
-        l4[e] = OP::sum2(pb, l4[e]);
-      }
-      pf[kq] = __builtin_bit_cast(opv8, u);
-    }
-    l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
-    if (any) {
-#pragma unroll
-      for (int c = 0; c < DBLK; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-    }
+            for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
+        });
   };
 
   // ---- prologue: K(0) stored (group A), V(0) in flight (group B), Q loaded

@@ -80,13 +80,6 @@ constexpr int kBN = 64;        // keys per KV tile: two 32-key MFMA blocks
 constexpr int kKB = kBN / 32;
 constexpr int kKT = kBN / 16;  // 16-key MFMA k-steps of the P.V contraction
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
-// A lane's sum of one tile's probabilities (32 keys) relative to the running
-// reference m_run may reach this before m_run moves to the running max, so
-// that no probability exceeds it: 2^15 keeps fp16 operands in range; bf16
-// operands (the fp32 exponent range) and the fp32 sums and accumulators
-// keep full relative precision far beyond 2^32.
-template <class OP> constexpr float sum_cap() { return 4294967296.0f; }
-template <> constexpr float sum_cap<OpFP16>() { return 32768.0f; }
 
 template <int HDIM>
 struct Cfg {
@@ -414,37 +407,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
-  // Mask (boundary tiles only), online softmax into the P operand, and
-  // the lazy rescale of O and l.
-  // Converts the tile's probabilities relative to neg_mc into the P operand
-  // and returns this lane's sum of the rounded values.
-  auto exp_tile = [&](float neg_mc) {
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
-      u32x4_t u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e], cmul, neg_mc));
-        const float p1 = fast_exp2(fmaf(s[kt >> 1][8 * (kt & 1) + 2 * e + 1], cmul, neg_mc));
-        // The dot product takes the converted pair itself: bit-casting an
-        // element of `u` back to a pair made hipcc (ROCm 7.2) feed the same
-        // register to every v_dot2c of the group.
-        const typename OP::v2 pb = OP::cvt2(p0, p1);
-        u[e] = __builtin_bit_cast(uint32_t, pb);
-        // l accumulates the rounded p that the P.V product uses
-        l4[e] = OP::sum2(pb, l4[e]);
-      }
-      pf[kt] = __builtin_bit_cast(opv8, u);
-    }
-    return (l4[0] + l4[1]) + (l4[2] + l4[3]);
-  };
-  // Mask (boundary tiles only), online softmax into the P operand, and
-  // the lazy rescale of O and l.  The probabilities are first taken
-  // against the running reference m_run with no max pass; only when a
-  // lane's sum of them exceeds kSumCap (so one may exceed the operand's
-  // range), or on a row's first visible tile (m_run = -inf), does the wave
-  // take the tile's max and move m_run to it.
+  // Mask (boundary tiles only), then the lazy online softmax into the P
+  // operand (lazy_softmax), and the rare rescale of O.
   auto softmax = [&](int kv0) {
     if (!tile_full(kv0)) {
       // Element r of key block kb holds key kv0 + 4*half + off, with the
@@ -462,29 +426,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
           if (off > hi || off < lo) s[kb][r] = -INFINITY;
         }
     }
-    float lt = exp_tile(m_run == -INFINITY ? 0.f : -m_run * cmul);
-    // (a NaN sum fails the comparison and takes the slow path too)
-    const bool raise = !(lt <= sum_cap<OP>()) || m_run == -INFINITY;
-    if (__ballot(raise) != 0ull) {  // wave-uniform, rare
-      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    lazy_softmax<OP, kKT>(
+        [&](int kt, int i) { return s[kt >> 1][8 * (kt & 1) + i]; }, cmul, m_run, l_run, pf, [&](float alpha) {
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
+          for (int c = 0; c < C::DBLK; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
-      const float mx = pair_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY || m_run == -INFINITY)
-                              ? (m_new == -INFINITY ? 1.f : 0.f)
-                              : fast_exp2((m_run - m_new) * cmul);
-      lt = exp_tile(m_new == -INFINITY ? 0.f : -m_new * cmul);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < C::DBLK; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-    }
-    l_run += lt;
+            for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
+        });
   };
 
   // ---- prologue: K(0) stored in stage 0 and K(1) in flight (group A),

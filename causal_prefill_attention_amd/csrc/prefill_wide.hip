@@ -39,6 +39,10 @@ constexpr int kXBN = 64;                   // keys per tile
 constexpr int kXKB = kXBN / 32;
 constexpr int kXKT = kXBN / 16;
 constexpr int kXBM = 32 * kXWaves;         // query rows per workgroup
+// Lazy-max threshold (log2 units): the probabilities against the running max
+// may reach 2^kXLazy before it moves.  (The prefill kernels' lazy_softmax,
+// which skips the max pass on most tiles, costs this kernel registers: the
+// 320/256 instance spilled 176 bytes instead of 104 and ran 20% slower.)
 constexpr float kXLazy = 8.0f;
 
 // DQK: head size of q and k (score contraction), DV: of v and out.
