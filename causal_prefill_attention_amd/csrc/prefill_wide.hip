@@ -60,6 +60,13 @@ struct WideCfg {
   static constexpr int K_TOTAL = kXBN * OCTS;
   static constexpr int V_TOTAL = (kXBN / 4) * VOCTS;
   static constexpr int K_CHUNKS = K_TOTAL / kXThreads;
+  // K staging: KTPR threads per row, each with KCPP 16-byte chunks of a row
+  // in each of KPASS row passes
+  static constexpr int KTPR = 8;
+  static constexpr int KROWS = kXThreads / KTPR;
+  static constexpr int KPASS = kXBN / KROWS;
+  static constexpr int KCPP = OCTS / KTPR;
+  static_assert(OCTS % KTPR == 0 && KPASS * KCPP == K_CHUNKS, "K staging map");
   static constexpr int V_UNITS = V_TOTAL / kXThreads;
   static_assert(K_CHUNKS * kXThreads == K_TOTAL && V_UNITS * kXThreads == V_TOTAL,
                 "every thread stages the same share");
@@ -134,16 +141,20 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   };
   u32x4_t kst[C::K_CHUNKS];
   u32x4_t vst[C::V_UNITS][4];
+  const int k_row = tid / C::KTPR, k_oct = tid % C::KTPR;
   auto gload_k = [&](int kv0) {
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<kvelem*>(kseq + tile_slot(kv0) * p.k_ts), 0, rows_of(kv0) * k_row_bytes,
         kRsrcWord3);
+    // thread t loads chunks (t % KTPR) + KTPR i of rows t / KTPR + KROWS pass:
+    // every KTPR lanes read 128 contiguous bytes of a row, and one offset
+    // register serves all of a thread's chunks (the rest are immediates)
 #pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int chunk = tid + i * kXThreads;
-      kst[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rk, (chunk / C::OCTS) * k_row_bytes + 16 * (chunk % C::OCTS), 0, 0);
-    }
+    for (int pass = 0; pass < C::KPASS; ++pass)
+#pragma unroll
+      for (int i = 0; i < C::KCPP; ++i)
+        kst[pass * C::KCPP + i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, (k_row + C::KROWS * pass) * k_row_bytes + 16 * (k_oct + C::KTPR * i), 0, 0);
   };
   auto gload_v = [&](int kv0) {
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -163,13 +174,13 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   // K row-major; Vᵀ in the Sᵀ accumulator's key order (inside each 16-key
   // group, positions 4..7 hold keys 8..11 and positions 8..11 keys 4..7).
   auto store_k = [&](int st) {
-    uint16_t* ks = kstage0 + st * C::K_ELEMS;
+    uint16_t* ks = kstage0 + st * C::K_ELEMS + k_row * C::KSTR + 8 * k_oct;
 #pragma unroll
-    for (int i = 0; i < C::K_CHUNKS; ++i) {
-      const int chunk = tid + i * kXThreads;
-      *reinterpret_cast<u32x4_t*>(ks + (chunk / C::OCTS) * C::KSTR + 8 * (chunk % C::OCTS)) =
-          kv_to_op(OP(), KVT(), kst[i]);
-    }
+    for (int pass = 0; pass < C::KPASS; ++pass)
+#pragma unroll
+      for (int i = 0; i < C::KCPP; ++i)
+        *reinterpret_cast<u32x4_t*>(ks + C::KROWS * pass * C::KSTR + 8 * C::KTPR * i) =
+            kv_to_op(OP(), KVT(), kst[pass * C::KCPP + i]);
   };
   auto store_v = [&](int st) {
     uint16_t* vs = vstage0 + st * C::V_ELEMS;
