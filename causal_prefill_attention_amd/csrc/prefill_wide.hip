@@ -39,10 +39,11 @@ constexpr int kXBN = 64;                   // keys per tile
 constexpr int kXKB = kXBN / 32;
 constexpr int kXKT = kXBN / 16;
 constexpr int kXBM = 32 * kXWaves;         // query rows per workgroup
-// Lazy-max threshold (log2 units): the probabilities against the running max
-// may reach 2^kXLazy before it moves.  (The prefill kernels' lazy_softmax,
-// which skips the max pass on most tiles, costs this kernel registers: the
-// 320/256 instance spilled 176 bytes instead of 104 and ran 20% slower.)
+// Softmax of the 320/256 instance: a max pass on every tile, the running max
+// moving when a tile's max exceeds it by more than 2^kXLazy (log2 units).
+// The 256-d instance uses lazy_softmax (no max pass on most tiles, 2%
+// faster); in the 320/256 instance its second exponent pass spills
+// registers and costs 5%.
 constexpr float kXLazy = 8.0f;
 
 // DQK: head size of q and k (score contraction), DV: of v and out.
@@ -254,6 +255,17 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
           if (!vis) s[kb][r] = -INFINITY;
         }
     }
+    auto rescale = [&](float alpha) {
+#pragma unroll
+      for (int c = 0; c < C::DBLK; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
+    };
+    if constexpr (DQK <= 256) {
+      lazy_softmax<OP, kXKT>([&](int kt, int i) { return s[kt >> 1][8 * (kt & 1) + i]; },
+                             cmul, m_run, l_run, pf, rescale);
+      return;
+    }
     float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < kXKB; ++kb)
@@ -283,12 +295,7 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
       pf[kt] = __builtin_bit_cast(opv8, u);
     }
     l_run = l_run * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
-    if (any) {
-#pragma unroll
-      for (int c = 0; c < C::DBLK; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-    }
+    if (any) rescale(alpha);
   };
 
   // ---- tile loop: tile j in stage j & 1.  Tile j + 1 moves in during
