@@ -47,6 +47,7 @@ KERNEL_SOURCES = [
     os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "prefill_fwd.hip"),
     os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "prefill_params.h"),
     os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "device_common.h"),
+    os.path.join(ROOT, "causal_prefill_attention_amd", "csrc", "prefill_work.h"),
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
