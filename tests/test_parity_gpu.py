@@ -181,6 +181,32 @@ def test_dtype_variants(qd, kvd):
         check(f"{w.name}_w{window}", to64(out), want)
 
 
+@pytest.mark.parametrize("kvd", ["bf16", "fp16"])
+@pytest.mark.parametrize("trend", ["rising", "falling"])
+def test_score_trends_through_the_lazy_reference(kvd, trend):
+    """Scores that rise by about 35 log2 units per 64-key tile make every
+    tile's probabilities overflow the lazy reference's cap (2^32 for bf16,
+    2^15 for fp16 operands), so the running max moves on every tile; scores
+    that fall as steeply leave every later tile's probabilities far below
+    the first tile's, down to exact zeros.  Both against the float64
+    oracle, with random V and two query-head signs per KV head."""
+    T, hq, hkv, d = 700, 4, 1, 128
+    w = workloads.custom(f"trend_{trend}_{kvd}", [T], hq, hkv, kv_dtype=kvd, seed=66)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    # s[i, j] = q[i] . k[j] = sign * 4.1 * j (raw units; scale 1/sqrt(128)
+    # makes that 0.52 log2 units per key)
+    slope = 4.1 if trend == "rising" else -4.1
+    j = torch.arange(T, dtype=torch.float64)
+    k = (slope * j / d)[:, None, None].expand(T, hkv, d).clone()
+    signs = torch.tensor([1.0, 1.0, -1.0, -1.0], dtype=torch.float64)
+    q = signs[None, :, None].expand(T, hq, d).clone()
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[kvd]
+    inp = dict(inp, q=q.to(torch.bfloat16), k=k.to(dt))
+    out = run_gpu(inp, hq, hkv, d, w.attn_scale, 0)
+    check(w.name, to64(out), oracle_of(inp, hq, hkv, w.attn_scale, 0))
+
+
 def test_window_one_returns_v_exactly_rounded():
     """W = 1: every query sees only itself, so out = bf16(v) exactly."""
     w = workloads.custom("w1", [300, 5], 4, 2, seed=41)
