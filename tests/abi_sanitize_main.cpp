@@ -135,6 +135,12 @@ int main() {
              ATTN_OK, "decode null workspace with a size");
   expect(attn_decode_paged_ws(&qd, &k, &v, &od, nullptr, 8, 2, 128, scale, 0, nullptr, 0,
                               nullptr) == ATTN_ERR_INVALID_ARG, "decode paged ws without a table");
+  expect(attn_decode_noalloc(&qd, &k, &v, &od, nullptr, 8, 2, 128, scale, 0, nullptr) ==
+             ATTN_ERR_INVALID_ARG, "no-alloc decode without key offsets");
+  expect(attn_decode_noalloc(&qd, &k, &v, &od, &cu, 8, 2, 128, scale, -5, nullptr) ==
+             ATTN_ERR_INVALID_ARG, "no-alloc decode negative window");
+  expect(attn_decode_noalloc(&qd, &k, &v, &od, &cu, 8, 3, 128, scale, 0, nullptr) ==
+             ATTN_ERR_INVALID_ARG, "no-alloc decode heads not a multiple of KV heads");
 
   // workspace sizes at the edges of their arguments
   const int64_t big[] = {-1, 0, 1, 63, 64, 65, 1 << 20, INT32_MAX, INT64_MAX / 4, INT64_MAX};

@@ -15,11 +15,11 @@ import subprocess
 
 import pytest
 
+from causal_prefill_attention_amd.build_lib import SOURCES  # the library's own list
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "causal_prefill_attention_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["prefill_fwd.hip", "prefill_wide.hip", "prefill_d512.hip", "decode_fwd.hip",
-           "attn_prefill.cpp"]
 # every sanitizer flag applies to the host compilation only
 ASAN_UBSAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
               "-Xarch_host", "-fno-sanitize-recover=all",
