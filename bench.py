@@ -52,11 +52,22 @@ KERNEL_SOURCES = [
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_of(text: str) -> str:
+    """Source text without // comments, trailing blanks and empty lines, so
+    that an edit of the comments does not count as a change of the kernel."""
+    out = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            out.append(code)
+    return "\n".join(out)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_of(f.read()).encode())
     return h.hexdigest()
 
 

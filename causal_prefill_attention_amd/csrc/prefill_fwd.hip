@@ -23,8 +23,15 @@
 //     [P(j-1) V(j-1), then S(j) = K(j) Q^T] while the other runs the softmax
 //     of its previous tile on the vector ALU, so the SIMD's matrix core and
 //     vector ALU are fed by different waves.  K(j) and V(j-1) stay in LDS for
-//     both slots; group A stages the next tiles (global loads in its matrix
-//     slot, LDS stores in its softmax slot) into the other LDS buffers.
+//     both slots; group A stages the next K tiles (in its softmax slot) and
+//     group B the next V tiles (after its matrix work) into the other LDS
+//     buffers.
+//   * Q enters through LDS: each wave loads its 32 rows whole (a lane per
+//     16-byte chunk, several rows per load instruction), rounds them into
+//     its own LDS slice and reads the MFMA operand layout back.
+//   * Folded grids (causal, no window, about one workgroup per CU): group A
+//     takes a sequence's 32-row block r and group B its mirror nb - 1 - r,
+//     so every workgroup sees about the same number of keys.
 //   * Both contractions run on the 32x32x16 MFMA of the K/V storage type
 //     (bf16 K/V: v_mfma_f32_32x32x16_bf16; fp16 K/V: ..._f16, so keys and
 //     values enter the products as stored) with fp32 accumulation; Q and P
