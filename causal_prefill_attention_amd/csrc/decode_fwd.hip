@@ -381,6 +381,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
 // heads: thread (col, pair) reads the split partials of two values, and a
 // wave's 32 columns read 128 contiguous bytes per value.
 constexpr int kMergeSlab = 16;
+constexpr int kMergeChunk = 16;  // splits combined per round of loads
 
 template <int HDIM>
 __global__ __launch_bounds__(kDThreads) void decode_merge_kernel(DecodeParams p) {
@@ -399,25 +400,38 @@ __global__ __launch_bounds__(kDThreads) void decode_merge_kernel(DecodeParams p)
   const int head = g * p.group + hcol;
   const float* base = p.partial + (int64_t)wid * p.n_splits * PF;
   const int n = p.n_splits;
-  // two rounds of independent loads: every split's max, then its sum and
-  // values (n <= kMaxSplits, so the unrolled loops cover every split)
-  float m[kMaxSplits];
-  float mx = -INFINITY;
+  // Splits in chunks of kMergeChunk, every load of a chunk issued before any
+  // is used (one memory latency per chunk), combined online: the sums so far
+  // are rescaled to the chunk's new max.  With n <= kMergeChunk this is the
+  // single combination relative to the overall max.
+  float mx = -INFINITY, den = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kMergeChunk) {
+    float m[kMergeChunk], l[kMergeChunk], v0[kMergeChunk], v1[kMergeChunk];
 #pragma unroll
-  for (int i = 0; i < kMaxSplits; ++i) {
-    m[i] = i < n ? base[(int64_t)i * PF + col] : -INFINITY;
-    mx = fmaxf(mx, m[i]);
-  }
-  float den = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxSplits; ++i) {
-    if (i < n) {
-      const float* part = base + (int64_t)i * PF;
-      const float w = m[i] == -INFINITY ? 0.f : fast_exp2((m[i] - mx) * p.score_mult);
-      den += w * part[32 + col];
-      a0 += w * part[64 + d * 32 + col];
-      a1 += w * part[64 + (d + 1) * 32 + col];
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const float* part = base + (int64_t)(i0 + j) * PF;
+      const bool in = i0 + j < n;
+      m[j] = in ? part[col] : -INFINITY;
+      l[j] = in ? part[32 + col] : 0.f;
+      v0[j] = in ? part[64 + d * 32 + col] : 0.f;
+      v1[j] = in ? part[64 + (d + 1) * 32 + col] : 0.f;
     }
+    float cm = mx;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) cm = fmaxf(cm, m[j]);
+    // (the sums are still zero while mx = -inf)
+    const float r = mx == -INFINITY ? 0.f : fast_exp2((mx - cm) * p.score_mult);
+    den *= r;
+    a0 *= r;
+    a1 *= r;
+#pragma unroll
+    for (int j = 0; j < kMergeChunk; ++j) {
+      const float w = m[j] == -INFINITY ? 0.f : fast_exp2((m[j] - cm) * p.score_mult);
+      den += w * l[j];
+      a0 += w * v0[j];
+      a1 += w * v1[j];
+    }
+    mx = cm;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   uint16_t* op = static_cast<uint16_t*>(p.out) + (int64_t)s * p.o_ts + (int64_t)head * p.o_hs;
