@@ -54,6 +54,14 @@
  * but no out-of-bounds access.  Setting ATTN_PREFILL_VALIDATE=1 in the
  * environment adds a debug-only host check of cu_seqlens that synchronises
  * the stream (never use it when timing or capturing).
+ *
+ * Grid shape.  For causal calls without a window whose grid would have at
+ * most one workgroup per compute unit, each workgroup pairs a sequence's
+ * 32-row query block r with block nb - 1 - r (nb blocks), so that every
+ * workgroup sees about the same number of keys; the output is bitwise the
+ * same as with the plain grid.  ATTN_PREFILL_FOLD=0 or =1 in the
+ * environment turns this off, or on wherever the head grouping allows it
+ * (for tests of both grids).
  */
 #ifndef ATTN_PREFILL_H
 #define ATTN_PREFILL_H
