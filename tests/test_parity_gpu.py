@@ -207,6 +207,19 @@ def test_score_trends_through_the_lazy_reference(kvd, trend):
     check(w.name, to64(out), oracle_of(inp, hq, hkv, w.attn_scale, 0))
 
 
+@pytest.mark.parametrize("qd", ["bf16", "fp32"])
+def test_fp16_kv_with_unit_scale(qd):
+    """fp16 K/V at scale 1: scores of about ±11 raw units (±16 log2 units)
+    move the fp16 operands' lazy reference (cap 2^15) on many tiles."""
+    w = workloads.custom(f"fp16_scale1_{qd}", [300, 77, 1, 130], 8, 2, q_dtype=qd,
+                         kv_dtype="fp16", seed=67, scale=1.0)
+    _announce(w.name)
+    inp = workloads.make_inputs(w)
+    for window in (0, 100):
+        out = run_gpu(inp, 8, 2, 128, w.attn_scale, window)
+        check(f"{w.name}_w{window}", to64(out), oracle_of(inp, 8, 2, w.attn_scale, window))
+
+
 def test_window_one_returns_v_exactly_rounded():
     """W = 1: every query sees only itself, so out = bf16(v) exactly."""
     w = workloads.custom("w1", [300, 5], 4, 2, seed=41)
