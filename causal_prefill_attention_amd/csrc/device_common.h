@@ -125,57 +125,13 @@ __device__ __forceinline__ void load_q_op(const T* qp, int half, float mult,
   for (int c = 0; c < DCH; ++c) qf[c] = to_op8<OP>(f[c], mult);
 }
 
-// The Qᵀ MFMA operands of one wave's 32 query rows, loaded through the
-// wave's own LDS slice (32 rows of `pitch` elements).  Whole rows are read
-// with 16-byte loads, one lane per 16-byte chunk (RPI rows per
-// instruction), so that every load instruction touches a few whole cache
-// lines; each chunk is multiplied by its row's multiplier (mult, or 0 for a
-// row at or past nvalid), rounded to the operand type and written to the
-// slice; then lane (col, half) reads back its operand chunks of row col.
-// Row r of the wave is token tok0 + row0 + r of qhead (token stride q_ts
-// elements); a row at or past nvalid reads token tok0 instead (a real row,
-// blanked by its zero multiplier).  The caller must keep other writers off
-// the slice until every wave of the workgroup has read its operands.
-template <int HDIM, class OP, class T>
-__device__ __forceinline__ void load_q_op_lds(const T* qhead, int64_t q_ts, int tok0, int row0,
-                                              int nvalid, float mult, uint16_t* slice,
-                                              int pitch, int lane, typename OP::v8* qf) {
-  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  constexpr int CPR = HDIM / EPC;           // chunks per row
-  static_assert(CPR <= 64 && 64 % CPR == 0, "a load instruction covers whole rows");
-  constexpr int RPI = 64 / CPR;             // rows per load instruction
-  constexpr int NI = 32 / RPI;              // load instructions per wave
-  const int rr = lane / CPR, ch = lane % CPR;
-  u32x4_t raw[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = RPI * i + rr;
-    const int tok = tok0 + (r < nvalid ? row0 + r : 0);
-    raw[i] = load16(qhead + (int64_t)tok * q_ts + EPC * ch);
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int r = RPI * i + rr;
-    const float m = r < nvalid ? mult : 0.f;
-    uint16_t* dst = slice + r * pitch + EPC * ch;
-    if constexpr (EPC == 8) {  // 16-bit elements (bf16)
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[2 * e] = __uint_as_float(raw[i][e] << 16);
-        f[2 * e + 1] = __uint_as_float(raw[i][e] & 0xffff0000u);
-      }
-      *reinterpret_cast<typename OP::v8*>(dst) = to_op8<OP>(f, m);
-    } else {  // fp32
-      u32x2_t u;
-      u[0] = __builtin_bit_cast(uint32_t, OP::cvt2(__uint_as_float(raw[i][0]) * m,
-                                                   __uint_as_float(raw[i][1]) * m));
-      u[1] = __builtin_bit_cast(uint32_t, OP::cvt2(__uint_as_float(raw[i][2]) * m,
-                                                   __uint_as_float(raw[i][3]) * m));
-      *reinterpret_cast<u32x2_t*>(dst) = u;
-    }
-  }
-  // the slice is the wave's own: LDS operations of one wave complete in order
+// Reads the Qᵀ MFMA operands of one wave's 32 query rows back from the
+// wave's own LDS slice (32 rows of `pitch` elements): lane (col, half) takes
+// its operand chunks of row col.  The slice is the wave's own, and LDS
+// operations of one wave complete in order, so a wave-level fence suffices.
+template <int HDIM, class OP>
+__device__ __forceinline__ void read_q_operand(const uint16_t* slice, int pitch, int lane,
+                                               typename OP::v8* qf) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -184,6 +140,67 @@ __device__ __forceinline__ void load_q_op_lds(const T* qhead, int64_t q_ts, int 
   for (int c = 0; c < HDIM / 16; ++c)
     qf[c] = *reinterpret_cast<const typename OP::v8*>(slice + col * pitch + 16 * c + 8 * half);
 }
+
+// The Qᵀ MFMA operands of one wave's 32 query rows, loaded through the
+// wave's own LDS slice, in two steps so that other work can run while the
+// loads are in flight.  issue() reads whole rows with 16-byte loads, one
+// lane per 16-byte chunk (RPI rows per instruction), so that every load
+// instruction touches a few whole cache lines; row r of the wave is token
+// tok0 + row0 + r of qhead (token stride q_ts elements), and a row at or
+// past nvalid reads token tok0 instead (a real row, blanked later).
+// finish() multiplies each chunk by its row's multiplier (mult, or 0 for a
+// row at or past nvalid), rounds it to the operand type, writes it to the
+// slice (the wave's own: no other wave may write it meanwhile) and reads the
+// operands back.
+template <int HDIM, class T>
+struct QRows {
+  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int CPR = HDIM / EPC;           // chunks per row
+  static_assert(CPR <= 64 && 64 % CPR == 0, "a load instruction covers whole rows");
+  static constexpr int RPI = 64 / CPR;             // rows per load instruction
+  static constexpr int NI = 32 / RPI;              // load instructions per wave
+  u32x4_t raw[NI];
+
+  __device__ __forceinline__ void issue(const T* qhead, int64_t q_ts, int tok0, int row0,
+                                        int nvalid, int lane) {
+    const int rr = lane / CPR, ch = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPI * i + rr;
+      const int tok = tok0 + (r < nvalid ? row0 + r : 0);
+      raw[i] = load16(qhead + (int64_t)tok * q_ts + EPC * ch);
+    }
+  }
+
+  template <class OP>
+  __device__ __forceinline__ void finish(int nvalid, float mult, uint16_t* slice, int pitch,
+                                         int lane, typename OP::v8* qf) const {
+    const int rr = lane / CPR, ch = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = RPI * i + rr;
+      const float m = r < nvalid ? mult : 0.f;
+      uint16_t* dst = slice + r * pitch + EPC * ch;
+      if constexpr (EPC == 8) {  // 16-bit elements (bf16)
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = __uint_as_float(raw[i][e] << 16);
+          f[2 * e + 1] = __uint_as_float(raw[i][e] & 0xffff0000u);
+        }
+        *reinterpret_cast<typename OP::v8*>(dst) = to_op8<OP>(f, m);
+      } else {  // fp32
+        u32x2_t u;
+        u[0] = __builtin_bit_cast(uint32_t, OP::cvt2(__uint_as_float(raw[i][0]) * m,
+                                                     __uint_as_float(raw[i][1]) * m));
+        u[1] = __builtin_bit_cast(uint32_t, OP::cvt2(__uint_as_float(raw[i][2]) * m,
+                                                     __uint_as_float(raw[i][3]) * m));
+        *reinterpret_cast<u32x2_t*>(dst) = u;
+      }
+    }
+    read_q_operand<HDIM, OP>(slice, pitch, lane, qf);
+  }
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float pair_max(float x);

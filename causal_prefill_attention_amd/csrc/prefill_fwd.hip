@@ -157,14 +157,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   typedef typename KVT::T kvelem;
   typedef typename OpOf<KVT>::T OP;  // operand type of both products
   typedef typename OP::v8 opv8;
-  // K stages [2][kBN][KSTR] then V^T stages [2][HDIM][VSTR] (operand bits).
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::K_ELEMS + 2 * C::V_ELEMS];
+  // K stages [2][kBN][KSTR], V^T stages [2][HDIM][VSTR] (operand bits), then
+  // one 32-row slice per wave (Q on the way in, O on the way out).
+  constexpr int QSTR = HDIM + 8;  // slice row pitch (16-bit elements)
+  __shared__ __attribute__((aligned(16)))
+  uint16_t smem[2 * C::K_ELEMS + 2 * C::V_ELEMS + kWaves * 32 * QSTR];
   uint16_t* const kstage0 = smem;
   uint16_t* const vstage0 = smem + 2 * C::K_ELEMS;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  uint16_t* const slice = smem + 2 * C::K_ELEMS + 2 * C::V_ELEMS + wave * 32 * QSTR;
   const int group = wave >> 2;                                   // 0 = A, 1 = B
   const int n_units = p.n_q_heads / HP;       // workgroups per tile slot (and piece)
   const int unit = blockIdx.x / n_units;      // slot, or slot * max_pieces + piece
@@ -214,16 +218,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   const int myq = wq0 + col;
   const int mypos = hist + myq;  // key position of this lane's query
 
-  // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7], loaded once the
-  // first tile's loads are in flight, through the wave's LDS slice (the
-  // epilogue's), with whole-row loads.
+  // ---- Q^T operand: lane holds q[myq, 16c + 8*half .. +7], read with
+  // whole-row loads through the wave's own LDS slice (QRows).
   opv8 qf[C::DCH];
   const qelem* const qhead = static_cast<const qelem*>(p.q) + (int64_t)head * p.q_hs;
-  constexpr int QSTR = HDIM + 8;  // Q / O slice row pitch in LDS (16-bit elements)
-  static_assert(kWaves * 32 * QSTR <= 2 * C::K_ELEMS + 2 * C::V_ELEMS, "Q slices fit");
-  auto load_q = [&]() {
-    load_q_op_lds<HDIM, OP>(qhead, p.q_ts, w.start, wq0, w.len - wq0, p.q_mult,
-                            smem + wave * 32 * QSTR, QSTR, lane, qf);
+  QRows<HDIM, qelem> qrows;
+  auto q_issue = [&]() { qrows.issue(qhead, p.q_ts, w.start, wq0, w.len - wq0, lane); };
+  auto q_finish = [&]() {
+    qrows.template finish<OP>(w.len - wq0, p.q_mult, slice, QSTR, lane, qf);
   };
 
   // ---- K/V tile movement (K by group A, V by group B).  Per-sequence bases
@@ -442,19 +444,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
         });
   };
 
-  // ---- prologue: K(0) stored in stage 0 and K(1) in flight (group A),
-  // V(0) in flight (group B).  K stage 0 overlaps Q slices, so it is
-  // written only once every wave holds its Q operand.
+  // ---- prologue: group A holds its Q operand, K(0) is in stage 0 and K(1)
+  // in flight; group B's Q and V(0) are in flight (B needs its Q only in
+  // slot 1, so it finishes it during A's first matrix slot).
+  // (The K/V loads go first: issuing Q first made hipcc keep about 30 more
+  // registers live across the tile loops.)
   if (group == 0) {
     gload_k(kv_start);
-    load_q();
-    __syncthreads();
+    q_issue();
+    q_finish();
     store_k(0);
     if (n_tiles > 1) gload_k(kv_start + kBN);
   } else {
     gload_v(kv_start);
-    load_q();
-    __syncthreads();
+    q_issue();
   }
   __syncthreads();
 
@@ -467,9 +470,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   // stages V, each at the end of its slot 2j-1 (A: softmax slot, B: matrix
   // slot, after its MFMAs are issued): store the tile loaded two slots
   // earlier, then issue the loads of the next one, so every load has two
-  // slots to arrive.  Both groups pass the same 2n + 2 barriers after the
-  // prologue.  Every wave runs every tile: a tile none of its rows can see
-  // is fully masked and contributes exact zeros.
+  // slots to arrive.  Both groups pass the same 2n + 1 barriers after the
+  // prologue's; group B's last P.V (slot 2n + 1) runs after the last one,
+  // beside group A's epilogue: from then on the waves only read the V stage
+  // and write their own slices.  Every wave runs every tile: a tile none of
+  // its rows can see is fully masked and contributes exact zeros.
   if (group == 0) {
     // Group A computes tiles [0, n_a) (n_a = n_tiles unless folded) and
     // stages K for all n_tiles: K(j + 1) stored and K(j + 2) issued in
@@ -512,8 +517,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
     }
     if (!FOLD || n_a == n_tiles) pv((n_tiles - 1) & 1);
     __syncthreads();
-    __syncthreads();
   } else {
+    q_finish();
     __syncthreads();
     // V(0) was loaded before the first barrier
     scores(0);
@@ -532,7 +537,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
       __syncthreads();
     }
     pv((n_tiles - 1) & 1);
-    __syncthreads();
   }
 
   const float l_tot = pair_sum(l_run);
@@ -558,11 +562,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   }
 
   // ---- epilogue: O / l -> bf16, rows of this sequence only.  The wave's
-  // 32 x HDIM tile goes through its own LDS slice (free after the last
-  // barrier) so that every global store writes whole 2*HDIM-byte rows.
+  // 32 x HDIM tile goes through its own LDS slice so that every global
+  // store writes whole 2*HDIM-byte rows.
   if (wave_live) {
     constexpr int OSTR = QSTR;
-    uint16_t* ob = smem + wave * 32 * OSTR;
+    uint16_t* ob = slice;
     // rows past the sequence are never stored; a row without any visible
     // key (malformed offsets only) is written as zeros
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
