@@ -78,8 +78,9 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   const int sl = wave & 3;      // column slice
   const int col = lane & 31;    // query column of this lane
   const int half = lane >> 5;
-  const int slot = blockIdx.x / p.n_q_heads;
-  const int head = blockIdx.x - slot * p.n_q_heads;
+  const int bid = dispatch_index(blockIdx.x);
+  const int slot = bid / p.n_q_heads;
+  const int head = bid - slot * p.n_q_heads;
   Work w = decode_work<kGBM, PAGED>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
   w.start = __builtin_amdgcn_readfirstlane(w.start);
@@ -327,7 +328,7 @@ template <class QT, class KVT>
 hipError_t launch_d512_one(PrefillParams p, hipStream_t stream) {
   const int64_t slots = (p.n_tokens + kGBM - 1) / kGBM + p.n_seqs;
   p.tile_slots = (int32_t)slots;
-  const uint64_t blocks = (uint64_t)slots * (uint64_t)p.n_q_heads;
+  const uint64_t blocks = dispatch_grid((uint64_t)slots * (uint64_t)p.n_q_heads);
   if (p.page_size > 0)
     hipLaunchKernelGGL((prefill_d512_kernel<QT, KVT, true>), dim3((uint32_t)blocks),
                        dim3(kGThreads), 0, stream, p);

@@ -171,19 +171,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_fwd_kernel(PrefillParams 
   uint16_t* const slice = smem + 2 * C::K_ELEMS + 2 * C::V_ELEMS + wave * 32 * QSTR;
   const int group = wave >> 2;                                   // 0 = A, 1 = B
   const int n_units = p.n_q_heads / HP;       // workgroups per tile slot (and piece)
-  // Dispatch order: workgroup b goes to XCD b mod 8, and an XCD starts its
-  // workgroups in order in fours, one per shader engine, each four once all
-  // four engines have a free CU, so the four that start together should
-  // take equally long.  Unsplit grids therefore permute every round of 32
-  // indices so that the k-th workgroup of a round on XCD x runs linear
-  // index 4q + k, q = x in even rounds and x ^ 6 in odd ones: with 8 units
-  // per slot, four head groups of one slot, the same four head groups on an
-  // XCD in every round (the KV heads its L2 holds), and over two rounds as
-  // much work on every XCD.  The grid is a whole number of rounds; indices
-  // past the work exit at once.
-  const unsigned bq = (blockIdx.x & 7u) ^ (6u * ((blockIdx.x >> 5) & 1u));
-  const int bid = SPLIT ? (int)blockIdx.x
-                        : (int)((blockIdx.x & ~31u) | (bq << 2) | ((blockIdx.x >> 3) & 3u));
+  // (unsplit grids run in dispatch order: dispatch_index)
+  const int bid = SPLIT ? (int)blockIdx.x : dispatch_index(blockIdx.x);
   const int unit = bid / n_units;             // slot, or slot * max_pieces + piece
   const int hbase = (bid - unit * n_units) * HP;
   const int head = hbase + (HP == 1 ? 0 : (wave & (HP - 1)));  // wave-uniform
@@ -667,9 +656,6 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
   }
 }
 
-// Unsplit grids are whole rounds of 32 workgroups (see the dispatch order).
-inline uint64_t round_up32(uint64_t n) { return (n + 31) & ~(uint64_t)31; }
-
 template <int HDIM, class QT, class KVT, bool PAGED>
 void launch_paged_or_not(PrefillParams p, uint64_t slots, hipStream_t stream) {
   if (p.piece_tiles == 0 && p.group % 4 == 0) {
@@ -679,7 +665,7 @@ void launch_paged_or_not(PrefillParams p, uint64_t slots, hipStream_t stream) {
     constexpr int bm = kBM / 4;
     const uint64_t slots4 = (uint64_t)((p.n_tokens + bm - 1) / bm + p.n_seqs);
     p.tile_slots = (int32_t)slots4;
-    const dim3 grid((uint32_t)round_up32(slots4 * (uint64_t)(p.n_q_heads / 4)));
+    const dim3 grid((uint32_t)dispatch_grid(slots4 * (uint64_t)(p.n_q_heads / 4)));
     if (p.fold && p.window == 0)
       hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 4, true>), grid,
                          dim3(kThreads), 0, stream, p);
@@ -698,7 +684,7 @@ void launch_paged_or_not(PrefillParams p, uint64_t slots, hipStream_t stream) {
                        dim3(256), 0, stream, p);
   } else {
     hipLaunchKernelGGL((prefill_fwd_kernel<HDIM, QT, KVT, PAGED, false, 1, false>),
-                       dim3((uint32_t)round_up32(slots * (uint64_t)p.n_q_heads)),
+                       dim3((uint32_t)dispatch_grid(slots * (uint64_t)p.n_q_heads)),
                        dim3(kThreads), 0, stream, p);
   }
 }

@@ -89,8 +89,9 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
   const int tid = threadIdx.x;
   const int lane = tid & (kXWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kXWave);
-  const int slot = blockIdx.x / p.n_q_heads;
-  const int head = blockIdx.x - slot * p.n_q_heads;
+  const int bid = dispatch_index(blockIdx.x);
+  const int slot = bid / p.n_q_heads;
+  const int head = bid - slot * p.n_q_heads;
   Work w = decode_work<kXBM, PAGED>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
   w.start = __builtin_amdgcn_readfirstlane(w.start);
@@ -365,7 +366,7 @@ template <int DQK, int DV, class QT, class KVT>
 hipError_t launch_wide_one(PrefillParams p, hipStream_t stream) {
   const int64_t slots = (p.n_tokens + kXBM - 1) / kXBM + p.n_seqs;
   p.tile_slots = (int32_t)slots;
-  const uint64_t blocks = (uint64_t)slots * (uint64_t)p.n_q_heads;
+  const uint64_t blocks = dispatch_grid((uint64_t)slots * (uint64_t)p.n_q_heads);
   if (p.page_size > 0)
     hipLaunchKernelGGL((prefill_wide_kernel<DQK, DV, QT, KVT, true>), dim3((uint32_t)blocks),
                        dim3(kXThreads), 0, stream, p);
