@@ -690,9 +690,10 @@ int run_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   const int64_t fit = split_bytes > 0 ? (int64_t)(workspace_bytes / (size_t)split_bytes) : 0;
   if (n_splits > fit) n_splits = (int)fit;
   if (n_splits < 2) n_splits = 1;
-  // the merge kernel of a split batch runs 8 workgroups per unit
+  // the merge kernel of a split batch runs 8 workgroups per unit; the decode
+  // grid is rounded up to a multiple of 32
   const int64_t blocks = n_splits > 1 && n_splits < 8 ? units * 8 : units * n_splits;
-  if (blocks * 256 >= ((int64_t)1 << 32))
+  if ((blocks + 31) * 256 >= ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "grid of %lld workgroups is too large", (long long)blocks);
   if (n_splits > 1) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace);

@@ -79,8 +79,10 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_fwd_kernel(DecodeParams p
 
   const int hblocks = (p.group + kDHeads - 1) / kDHeads;
   const int per_seq = hblocks * p.n_kv_heads;  // units of one sequence
-  const int split = blockIdx.x % p.n_splits;
-  const int order = blockIdx.x / p.n_splits;
+  const int bid = dispatch_index(blockIdx.x);
+  const int split = bid % p.n_splits;
+  const int order = bid / p.n_splits;
+  if (order >= p.n_seqs * per_seq) return;  // past the work (uniform)
   const int rank = order / per_seq;
   const int sub = order - rank * per_seq;
   const int hb = sub % hblocks;
@@ -442,7 +444,7 @@ template <class QT, class KVT>
 hipError_t launch_decode_one(const DecodeParams& p, hipStream_t stream) {
   const int64_t hblocks = (p.group + kDHeads - 1) / kDHeads;
   const uint64_t units = (uint64_t)p.n_seqs * (uint64_t)p.n_kv_heads * (uint64_t)hblocks;
-  const uint64_t blocks = units * (uint64_t)p.n_splits;
+  const uint64_t blocks = dispatch_grid(units * (uint64_t)p.n_splits);
   if (p.page_size > 0)
     hipLaunchKernelGGL((decode_fwd_kernel<128, QT, KVT, true>), dim3((uint32_t)blocks),
                        dim3(kDThreads), 0, stream, p);

@@ -33,23 +33,6 @@ struct Work {
 // about the same number of causal keys; rank 0 (the first block with the
 // last, the heaviest pair) comes first.  q0 is block r, q0_b the mirror;
 // they coincide for the middle block of an odd nb.
-// Dispatch order.  Workgroup b of a grid goes to XCD b mod 8, and an XCD
-// starts its workgroups in order, four at a time (one per shader engine),
-// each four once all four engines have a free CU; so the four that start
-// together should take equally long.  An unsplit prefill grid is a whole
-// number of rounds of 32 workgroups (dispatch_grid), and workgroup b runs
-// linear index dispatch_index(b): in each round, the k-th workgroup on XCD
-// x runs index 4q + k, q = x in even rounds and x ^ 6 in odd ones.  With 8
-// (or 16) workgroups per slot the four are head groups of one slot, an XCD
-// keeps the same heads in every round (with 8 per slot: the KV heads its L2
-// holds), and over two rounds every XCD gets as much work.  Indices past
-// the work decode as invalid and exit at once.
-__device__ __forceinline__ int dispatch_index(unsigned b) {
-  const unsigned q = (b & 7u) ^ (6u * ((b >> 5) & 1u));
-  return (int)((b & ~31u) | (q << 2) | ((b >> 3) & 3u));
-}
-inline uint64_t dispatch_grid(uint64_t n) { return (n + 31) & ~(uint64_t)31; }
-
 template <int BM, bool PAGED, bool FOLD = false>
 __device__ Work decode_work(const PrefillParams& p, int slot) {
   const int lane = threadIdx.x & (kWorkWave - 1);
