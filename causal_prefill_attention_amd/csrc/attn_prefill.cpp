@@ -527,23 +527,34 @@ int run_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v
   p.piece_tiles = sp.piece_tiles;
   p.max_pieces = sp.max_pieces;
   p.partial = sp.piece_tiles > 0 ? static_cast<float*>(workspace) : nullptr;
-  // A causal grid of at most one workgroup (four query heads of a KV head,
-  // 64 rows each) per CU finishes with its heaviest query tile, which sees
-  // twice the keys of the average one; folded, every workgroup pairs a
-  // sequence's 32-row block r with block nb - 1 - r.  Sum over sequences of
-  // ceil(len / 64) is at most ceil(T / 64) + n_seqs - 1.
+  // A causal grid of at most one workgroup per CU finishes with its
+  // heaviest query tile, which sees twice the keys of the average one;
+  // folded, every workgroup pairs a sequence's row block r with block
+  // nb - 1 - r: 32-row blocks of four query heads of a KV head (64 rows
+  // each per workgroup) for the 64-d and 128-d kernel, 64-row blocks of one
+  // head (128 rows per workgroup) for the 512-d kernel.  Sum over sequences
+  // of ceil(len / rows) is at most ceil(T / rows) + n_seqs - 1.
   // ATTN_PREFILL_FOLD=0 / =1 turns folding off / on wherever the shape
   // allows it (for tests of both grids on one shape).
   p.fold = 0;
-  if (sp.piece_tiles == 0 && sliding_window == 0 && head_dim == head_dim_v &&
-      (head_dim == 64 || head_dim == 128) && p.group % 4 == 0) {
+  int64_t fold_rows = 0, fold_units = 0;
+  if (sp.piece_tiles == 0 && sliding_window == 0 && head_dim == head_dim_v) {
+    if ((head_dim == 64 || head_dim == 128) && p.group % 4 == 0) {
+      fold_rows = 64;
+      fold_units = n_q_heads / 4;
+    } else if (head_dim == 512) {
+      fold_rows = 128;
+      fold_units = n_q_heads;
+    }
+  }
+  if (fold_rows > 0) {
     const char* force = getenv("ATTN_PREFILL_FOLD");
     if (force != nullptr && (force[0] == '0' || force[0] == '1')) {
       p.fold = force[0] == '1';
     } else {
-      const int64_t pairs = (T + 63) / 64 + cu_q->n_seqs - 1;
+      const int64_t pairs = (T + fold_rows - 1) / fold_rows + cu_q->n_seqs - 1;
       const int64_t cus = device_cus();
-      if (cus > 0 && pairs * (n_q_heads / 4) <= cus) p.fold = 1;
+      if (cus > 0 && pairs * fold_units <= cus) p.fold = 1;
     }
   }
   const hipError_t e = attnp::launch_prefill(p, head_dim, head_dim_v, (attnp::DType)q->dtype,

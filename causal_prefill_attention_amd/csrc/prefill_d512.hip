@@ -8,29 +8,36 @@
 // prefill of atlas PR #69.
 //
 // Design (ours, for CDNA4): a 512-d head would need 256 fp32 accumulator
-// and 128 Q operand registers in one 32-row wave, beyond one wave's
-// budget.  The head is split by columns instead, and the split is laid over
-// the 128-d kernel's ping-pong:
-//   * Eight waves in two groups, A (waves 0-3) and B (4-7), each group one
-//     32-row query block (64 rows per workgroup).  Wave w of a group owns
-//     columns [128w, 128w + 128) of Q, K, V and out, so waves w and w + 4 --
-//     one SIMD -- share that column slice of every K/V tile.
-//   * Per 32-key tile a wave forms partial scores Sᵀ_w = K_w Q_wᵀ from its
-//     columns (8 MFMAs, 32x32x16 in the K/V storage type) and writes them to its group's LDS
-//     exchange; in the group's next slot every wave sums the four partials
-//     in the same order (so all four hold the same fp32 scores), runs the
-//     same online softmax, and later accumulates Oᵀ_w += Vᵀ_w Pᵀ for its 128
-//     output columns (8 MFMAs).  No MFMA work is repeated.
-//   * The groups run in anti-phase as in the 128-d kernel: in one slot group
-//     A issues its MFMAs (P.V of the previous tile, then the partial scores
-//     of this one) while group B runs its exchange and softmax, and the
-//     next slot the other way round, so the matrix core of each SIMD is fed
-//     by one wave while the vector ALU works for the other.
-//   * Group A stages the K column slices and group B the V slices through
-//     registers into two LDS stages (rows of 128 elements, 16-byte chunks of row
-//     r at position chunk ^ (r & 15)); Vᵀ operands come from the transposing
-//     LDS read ds_read_b64_tr_b16.  LDS: 128 KiB of K/V stages and 32 KiB of
-//     exchange.
+// and 128 Q operand registers in one 32-row wave, beyond the budget of two
+// waves per SIMD.  The head is split into two column halves instead, laid
+// over the 128-d kernel's ping-pong:
+//   * Eight waves in two groups, A (waves 0-3) and B (4-7), each group 64
+//     query rows (128 per workgroup): wave w of a group runs the 32-row
+//     block (w >> 1) & 1 on columns [256 h, 256 h + 256), h = w & 1, of Q,
+//     K, V and out.  Waves w and w + 4 -- one SIMD -- read the same column
+//     half of every K/V tile.
+//   * Per 32-key tile a wave forms partial scores Sᵀ_h = K_h Q_hᵀ from its
+//     half (16 MFMAs, 32x32x16 in the K/V storage type) and writes them to
+//     LDS; in the group's next slot it adds its partner's (same rows, other
+//     half: the two sums are the same fp32 numbers, a + b = b + a), runs the
+//     online softmax (both partners take the same decisions on the same
+//     scores) and later accumulates Oᵀ_h += Vᵀ_h Pᵀ for its 256 output
+//     columns (16 MFMAs).  No MFMA work is repeated.
+//   * The groups run in anti-phase as in the 128-d kernel: in one slot
+//     group A issues its MFMAs (the partial scores of tile j, then P.V of
+//     tile j - 1) while group B adds partials and runs its softmax, and the
+//     next slot the other way round.
+//   * K and V tiles go straight from memory into LDS (buffer loads to LDS,
+//     one 1 KiB row per instruction, 16-byte chunk c of row r at position
+//     c ^ (r & 15) for K, c ^ 2 (r & 7) for V, so that the K operand reads
+//     (16 rows, 16 bytes each) and the transposing Vᵀ reads (4 rows, 32
+//     bytes each, per 16 lanes) meet no bank twice): group A moves K, group B moves V, each load issued two
+//     slots before the tile is read and waited for before the barrier that
+//     publishes it, with no staging registers.  Vᵀ operands come from the
+//     transposing LDS read ds_read_b64_tr_b16.  LDS: two K and two V
+//     stages (128 KiB) and the partial scores of the eight waves (32 KiB).
+//   * Folded grids (causal, no window, about one workgroup per CU): group A
+//     takes a sequence's 64-row block r and group B its mirror nb - 1 - r.
 #include <hip/hip_runtime.h>
 #include <climits>
 #include <stdint.h>
@@ -49,65 +56,83 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kGWave = 64;
 constexpr int kGWaves = 8;                  // two groups of four
 constexpr int kGThreads = kGWave * kGWaves;
-constexpr int kGSlices = 4;                 // column slices (one wave per group each)
-constexpr int kGSlice = 512 / kGSlices;     // 128 columns per slice
-constexpr int kGBM = 64;                    // query rows per workgroup (32 per group)
+constexpr int kGD = 512;                    // head size
+constexpr int kGHalf = kGD / 2;             // columns per wave
+constexpr int kGBM = 128;                   // query rows per workgroup (64 per group)
 constexpr int kGBN = 32;                    // keys per tile: one 32-key score block
 constexpr int kGKQ = kGBN / 16;             // 16-key P.V steps per tile
+constexpr int kGTile = kGBN * kGD;          // elements of one K or V stage
 
-template <class QT, class KVT, bool PAGED>
+// FOLD: group A runs the 64-row block r of a sequence and group B its
+// mirror nb - 1 - r (causal, no window); group B, the later block, sees at
+// least as many key tiles, and group A stops its matrix and softmax work
+// after its own last key tile (it keeps moving K and passing the barriers).
+template <class QT, class KVT, bool PAGED, bool FOLD>
 __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParams p) {
-  constexpr int CPR = kGSlice / 8;            // 16-byte chunks per slice row
-  constexpr int DCH = kGSlice / 16;           // score k-steps per slice
-  constexpr int DBLK = kGSlice / 32;          // output blocks per slice
-  constexpr int TILE = kGBN * kGSlice;        // elements of one K or V slice tile
-  constexpr int LOADS = kGBN * CPR / kGWave;  // 16-byte chunks per lane per tile
+  constexpr int DCH = kGHalf / 16;   // score k-steps per half
+  constexpr int DBLK = kGHalf / 32;  // output blocks per half
+  constexpr int BMG = kGBM / 2;      // query rows per group
   typedef typename QT::T qelem;
   typedef typename KVT::T kvelem;
   typedef typename OpOf<KVT>::T OP;  // operand type of both products
   typedef typename OP::v8 opv8;
 
-  // [stage][slice][K, V][TILE] operand elements, then the exchange [group][slice][r/4][lane]
-  __shared__ __attribute__((aligned(16))) uint16_t kvs[2 * kGSlices * 2 * TILE];
-  __shared__ __attribute__((aligned(16))) f32x4_t xch[2 * kGSlices * 4 * kGWave];
+  // K stages 0, 1 then V stages 0, 1 ([32 rows][512] operand elements), then
+  // the partial scores [wave][r/4][lane]
+  __shared__ __attribute__((aligned(16))) uint16_t kvs[4 * kGTile];
+  __shared__ __attribute__((aligned(16))) f32x4_t xch[kGWaves * 4 * kGWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kGWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kGWave);
-  const int group = wave >> 2;  // 0 = A (stages K), 1 = B (stages V)
-  const int sl = wave & 3;      // column slice
-  const int col = lane & 31;    // query column of this lane
+  const int group = wave >> 2;      // 0 = A (moves K), 1 = B (moves V)
+  const int blk = (wave >> 1) & 1;  // 32-row block of the group
+  const int hf = wave & 1;          // column half
+  const int col = lane & 31;        // query column of this lane
   const int half = lane >> 5;
   const int bid = dispatch_index(blockIdx.x);
   const int slot = bid / p.n_q_heads;
   const int head = bid - slot * p.n_q_heads;
-  Work w = decode_work<kGBM, PAGED>(p, slot);
+  Work w = decode_work<FOLD ? BMG : kGBM, PAGED, FOLD>(p, slot);
   if (!w.valid) return;  // uniform across the workgroup
   w.start = __builtin_amdgcn_readfirstlane(w.start);
   w.len = __builtin_amdgcn_readfirstlane(w.len);
   w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
+  w.q0_b = __builtin_amdgcn_readfirstlane(w.q0_b);
   w.kstart = __builtin_amdgcn_readfirstlane(w.kstart);
   w.seq = __builtin_amdgcn_readfirstlane(w.seq);
   w.klen = __builtin_amdgcn_readfirstlane(w.klen);
 
   const int kvh = head / p.group;
   const int hist = w.klen - w.len;  // queries are the last len key positions
-  const int q_end = min(w.len, w.q0 + kGBM);
+  // key range of the workgroup: the whole 128-row tile, or, folded, group
+  // B's block (which starts at key 0 and ends last)
+  const int qb = FOLD ? w.q0_b : w.q0;
+  const int q_end = min(w.len, qb + (FOLD ? BMG : kGBM));
   const int kv_hi = min(max(hist + q_end, 0), w.klen);
   const int kv_lo = p.window > 0 ? min(max(0, hist + w.q0 - p.window + 1), kv_hi) : 0;
   const int kv_start = kv_lo - kv_lo % kGBN;
   const int n_tiles = max(1, (kv_hi - kv_start + kGBN - 1) / kGBN);
-  const int wq0 = w.q0 + 32 * group;  // this group's query block
+  const bool a_live = !FOLD || w.q0 != w.q0_b;
+  int n_a = n_tiles;
+  if (FOLD) {
+    const int a_hi = min(max(hist + min(w.len, w.q0 + BMG), 0), w.klen);
+    n_a = a_live ? max(1, (a_hi + kGBN - 1) / kGBN) : 0;
+  }
+  // first row of this wave (a folded idle group A gets rows past the sequence)
+  const int wq0 = (FOLD ? (group == 0 ? (a_live ? w.q0 : w.len) : w.q0_b) : w.q0 + BMG * group) +
+                  32 * blk;
   const int wq_last = min(wq0 + 31, w.len - 1);
   const int myq = wq0 + col;
   const int mypos = hist + myq;
-  const int d0 = sl * kGSlice;  // first column of this wave's slice
+  const int d0 = kGHalf * hf;  // first column of this wave's half
 
-  // ---- K (group A) or V (group B) slice tiles: lane moves chunk
-  // (lane % CPR) of rows 4i + lane / CPR
+  // ---- K (group A) or V (group B) tiles straight into LDS: wave i of the
+  // group moves rows 8i .. 8i + 7, one row per load, lane l the chunk that
+  // goes to position l of the row
   const kvelem* src = group == 0
-      ? static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts + (int64_t)kvh * p.k_hs + d0
-      : static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts + (int64_t)kvh * p.v_hs + d0;
+      ? static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts + (int64_t)kvh * p.k_hs
+      : static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts + (int64_t)kvh * p.v_hs;
   const int64_t src_ts = group == 0 ? p.k_ts : p.v_ts;
   const int row_bytes = (int)(src_ts * (int64_t)sizeof(kvelem));
   auto tile_slot = [&](int kv0) -> int64_t {
@@ -117,85 +142,114 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
     const int page = min(max(row[idx], 0), p.n_pages - 1);
     return (int64_t)page * p.page_size + (kv0 - idx * p.page_size);
   };
-  u32x4_t st_regs[LOADS];
-  auto gload = [&](int kv0) {
+  auto move = [&](int kv0, int st) {
     // rows past the last visible key read as zero (buffer range)
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kv_hi - kv0, kGBN)));
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<kvelem*>(src + tile_slot(kv0) * src_ts), 0, rows * row_bytes, kRsrcWord3);
+    uint16_t* stage = kvs + (2 * group + st) * kGTile;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int row = i * (kGWave / CPR) + lane / CPR;
-      st_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(r, row * row_bytes + 16 * (lane % CPR),
-                                                         0, 0);
+    for (int i = 0; i < kGBN / 4; ++i) {
+      const int row = (kGBN / 4) * (wave & 3) + i;
+      const int key = group == 0 ? (row & 15) : 2 * (row & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(stage + row * kGD), 16,
+          row * row_bytes + 16 * (lane ^ key), 0, 0, 0);
     }
   };
-  auto kslice = [&](int st) { return kvs + ((st * kGSlices + sl) * 2 + 0) * TILE; };
-  auto vslice = [&](int st) { return kvs + ((st * kGSlices + sl) * 2 + 1) * TILE; };
-  auto lstore = [&](int st) {  // group A: K stage st; group B: V stage st
-    uint16_t* dst = group == 0 ? kslice(st) : vslice(st);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int row = i * (kGWave / CPR) + lane / CPR;
-      const int pos = (lane % CPR) ^ (row & 15);
-      *reinterpret_cast<u32x4_t*>(dst + row * kGSlice + 8 * pos) = kv_to_op(OP(), KVT(), st_regs[i]);
-    }
-  };
+  // the loads this wave issued have reached LDS (before the barrier that
+  // publishes them)
+  auto landed = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  const uint16_t* const kst0 = kvs;
+  const uint16_t* const vst0 = kvs + 2 * kGTile;
 
-  // ---- Qᵀ operand of this wave's slice: lane holds q[myq, d0 + 16c + 8*half ..]
+  // ---- Qᵀ operand of this wave's half: lane holds q[myq, d0 + 16c + 8*half ..]
   opv8 qf[DCH];
   const qelem* const qrow = static_cast<const qelem*>(p.q) +
                             (int64_t)(w.start + (myq < w.len ? myq : 0)) * p.q_ts +
                             (int64_t)head * p.q_hs + d0;
   const float qmul = myq < w.len ? p.q_mult : 0.f;
 
-  // ---- per-wave state (the four waves of a group keep the same m and l)
+  // ---- per-wave state (the two waves of a block keep the same m and l)
   f32x16_t o[DBLK];
 #pragma unroll
   for (int c = 0; c < DBLK; ++c) o[c] = (f32x16_t){};
+  f32x16_t sc;
   opv8 pf[kGKQ];
   float m_run = -INFINITY;
   float l_run = 0.f;
   const float cmul = p.score_mult;
-  f32x4_t* const xg = xch + group * kGSlices * 4 * kGWave;  // this group's exchange
-  f32x4_t* const xw = xg + sl * 4 * kGWave;                   // this wave's partial
+  f32x4_t* const xw = xch + wave * 4 * kGWave;              // this wave's partial
+  const f32x4_t* const xp = xch + (wave ^ 1) * 4 * kGWave;  // its partner's
 
-  // partial Sᵀ = K_w Q_wᵀ of the tile in K stage st, to the exchange
+  // LDS operand addresses.  For a lane's fixed row only the low bits of the
+  // k-step index meet the swizzle, so each lane keeps a few base addresses
+  // per operand and the rest of every address is an immediate offset.
+  //   K, score step c (0..15), row col: chunk 32 hf + 2c + half at position
+  //     chunk ^ (col & 15), element col*512 + 256 hf + 8 (half ^ (col & 1)) +
+  //     16 ((c & 7) ^ y) + 128 (c >> 3), y = (col >> 1) & 7.
+  //   V, P.V step kq, output block c (0..7), read r: row 16 kq + 8 r + t
+  //     (t = 4 half + j / 4, j = lane & 15), columns d0 + 32 c + 16 g +
+  //     4 (j & 3) (g = bit 4 of the lane): chunk 32 hf + 4c + 2g + (j & 3) / 2
+  //     at position chunk ^ 2t, element kq*8192 + r*4096 + t*512 + 256 hf +
+  //     16 (g ^ (t & 1)) + 8 ((j & 3) / 2) + 4 (j & 1) + 32 ((c & 3) ^ k) +
+  //     128 (c >> 2), k = t / 2.
+  // (The bases are formed again at every tile from an opaque copy of the
+  // lane index, a few vector instructions, rather than kept live across the
+  // tile loop: the loop holds 216 registers of Q, O, S and P already.)
+  auto k_bases = [&](int* kaddr) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int cl = ln & 31, hl = ln >> 5, y = (cl >> 1) & 7;
+    const int kb = cl * kGD + 256 * hf + 8 * (hl ^ (cl & 1));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kaddr[c] = kb + 16 * (c ^ y);
+  };
+  auto v_bases = [&](int* vaddr) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int g = (ln >> 4) & 1, j = ln & 15, hl = ln >> 5;
+    const int t = 4 * hl + (j >> 2);
+    const int vb = t * kGD + 256 * hf + 16 * (g ^ (t & 1)) + 8 * ((j & 3) >> 1) + 4 * (j & 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vaddr[c] = vb + 32 * (c ^ (t >> 1));
+  };
+
+  // partial Sᵀ_h = K_h Q_hᵀ of the tile in K stage st
   auto scores = [&](int st) {
-    const uint16_t* kt = kslice(st);
-    f32x16_t sc = (f32x16_t){};
+    const uint16_t* kt = kst0 + st * kGTile;
+    int kaddr[8];
+    k_bases(kaddr);
+    sc = (f32x16_t){};
 #pragma unroll
     for (int c = 0; c < DCH; ++c) {
-      const int pos = (2 * c + half) ^ (col & 15);
-      const opv8 a = *reinterpret_cast<const opv8*>(kt + col * kGSlice + 8 * pos);
+      const opv8 a = *reinterpret_cast<const opv8*>(kt + kaddr[c & 7] + 128 * (c >> 3));
       sc = OP::mfma(a, qf[c], sc);
     }
+  };
+  auto publish = [&]() {
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
       xw[r4 * kGWave + lane] = (f32x4_t){sc[4 * r4], sc[4 * r4 + 1], sc[4 * r4 + 2],
                                          sc[4 * r4 + 3]};
   };
-  // Oᵀ_w += Vᵀ_w Pᵀ for the tile in V stage st.  MFMA k-index 8*half + e of
+  // Oᵀ_h += Vᵀ_h Pᵀ for the tile in V stage st.  MFMA k-index 8*half + e of
   // step kq is key 16*kq + 8*(e / 4) + 4*half + e % 4 (the Sᵀ accumulator's
   // order): two transposing reads give keys +0..3 and +8..11 (+4*half).
   auto pv = [&](int st) {
-    const uint16_t* vt = vslice(st);
-    const int grp16 = (lane >> 4) & 1;  // 16-column half of the 32-row block
-    const int j = lane & 15;
+    const uint16_t* vt = vst0 + st * kGTile;
+    int vaddr[4];
+    v_bases(vaddr);
 #pragma unroll
     for (int kq = 0; kq < kGKQ; ++kq) {
 #pragma unroll
       for (int c = 0; c < DBLK; ++c) {
         s16x4_t part[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int row = 16 * kq + 8 * r + 4 * half + (j >> 2);
-          const int d = 32 * c + 16 * grp16 + 4 * (j & 3);
-          const int pos = (d >> 3) ^ (row & 15);
+        for (int r = 0; r < 2; ++r)
           part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(vt + row * kGSlice + 8 * pos +
-                                                           (d & 7)));
-        }
+              (__attribute__((address_space(3))) s16x4_t*)(vt + kq * 8192 + 4096 * r +
+                                                           vaddr[c & 3] + 128 * (c >> 2)));
         u32x4_t u;
         u[0] = __builtin_bit_cast(u32x2_t, part[0])[0];
         u[1] = __builtin_bit_cast(u32x2_t, part[0])[1];
@@ -205,16 +259,83 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
       }
     }
   };
-  // the group's four partials summed in slice order, masks, online softmax
+  // Matrix slot of tile j when both P(j-1)V(j-1) and S(j) are due, as one
+  // straight-line block: the 16 P.V MFMAs (P dies with them), then the 16
+  // partial-score MFMAs, every LDS operand read kAhead MFMAs ahead (a Vᵀ
+  // operand is two transposing reads), the order pinned.
+  auto matrix = [&](int kst_i, int vst_i) {
+    const uint16_t* kt = kst0 + kst_i * kGTile;
+    const uint16_t* vt = vst0 + vst_i * kGTile;
+    constexpr int NPV = kGKQ * DBLK, N = NPV + DCH;
+    int kaddr[8], vaddr[4];
+    v_bases(vaddr);
+    k_bases(kaddr);
+    auto operand = [&](int i) -> opv8 {
+      if (i >= NPV) {
+        const int c = i - NPV;
+        return *reinterpret_cast<const opv8*>(kt + kaddr[c & 7] + 128 * (c >> 3));
+      }
+      const int kq = i / DBLK, c = i % DBLK;
+      s16x4_t part[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vt + kq * 8192 + 4096 * r +
+                                                         vaddr[c & 3] + 128 * (c >> 2)));
+      u32x4_t u;
+      u[0] = __builtin_bit_cast(u32x2_t, part[0])[0];
+      u[1] = __builtin_bit_cast(u32x2_t, part[0])[1];
+      u[2] = __builtin_bit_cast(u32x2_t, part[1])[0];
+      u[3] = __builtin_bit_cast(u32x2_t, part[1])[1];
+      return __builtin_bit_cast(opv8, u);
+    };
+    constexpr int kAhead = 4;
+    static_assert(kAhead < NPV && kAhead < DCH, "look-ahead within each product");
+    opv8 buf[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) buf[i] = operand(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const opv8 a = buf[i % kAhead];
+      if (i + kAhead < N) buf[i % kAhead] = operand(i + kAhead);
+      if (i < NPV) {
+        o[i % DBLK] = OP::mfma(a, pf[i / DBLK], o[i % DBLK]);
+      } else {
+        const int c = i - NPV;
+        sc = OP::mfma(a, qf[c], c == 0 ? (f32x16_t){} : sc);
+      }
+    }
+    // pin the order: the first kAhead operands' reads, then (MFMA, the reads
+    // of the operand kAhead further on) pairs, then the last kAhead MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < NPV - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = NPV - kAhead; i < N - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+  };
+  // End of a matrix slot: the partial written, then the barrier, without
+  // waiting for this wave's K/V loads to LDS still in flight (they are waited
+  // for at the end of the next slot, before the stage is read).
+  auto end_matrix_slot = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // End of a softmax slot that leaves K/V loads in flight (group B's).
+  auto end_soft_slot = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // own partial plus the partner's (both read back: the scores leave the
+  // registers after the matrix slot), masks, online softmax
   auto softmax = [&](int kv0) {
-    f32x16_t sc;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      f32x4_t acc = xg[r4 * kGWave + lane];
+      const f32x4_t a = xw[r4 * kGWave + lane];
+      const f32x4_t b = xp[r4 * kGWave + lane];
 #pragma unroll
-      for (int v = 1; v < kGSlices; ++v) acc += xg[(v * 4 + r4) * kGWave + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[4 * r4 + e] = acc[e];
+      for (int e = 0; e < 4; ++e) sc[4 * r4 + e] = a[e] + b[e];
     }
     const bool full = (kv0 + kGBN - 1 <= hist + wq0) &&
                       (p.window == 0 || kv0 >= hist + wq_last - p.window + 1);
@@ -239,73 +360,84 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
         });
   };
 
-  // ---- prologue: K(0) stored (group A), V(0) in flight (group B), Q loaded
-  // once the first tile's loads are issued
-  gload(kv_start);
+  // ---- prologue: K(0) and K(1) (group A) or V(0) (group B) in LDS, Q in
+  // registers
+  move(kv_start, 0);
+  if (group == 0 && n_tiles > 1) move(kv_start + kGBN, 1);
   load_q_op<DCH, OP>(qrow, half, qmul, qf);
-  if (group == 0) {
-    lstore(0);
-    if (n_tiles > 1) gload(kv_start + kGBN);
-  }
+  landed();
   __syncthreads();
 
   // ---- ping-pong slots (the 128-d kernel's schedule).  In slot 2j group A
-  // runs its matrix work for tile j (P(j-1)V(j-1), then partial S(j) to its
-  // exchange) while group B runs softmax(j-1) from its exchange; in slot
-  // 2j+1 the other way round.  K(j) (stage j&1) is read in slots 2j and
-  // 2j+1, V(j) (stage j&1) in slots 2j+2 and 2j+3.  Group A writes K(j+1)
-  // in its softmax slot 2j+1, group B writes V(j) after its matrix work in
-  // slot 2j+1; each load has two slots to arrive.  A group's exchange is
-  // written in its matrix slot and read in its next slot, after the
-  // barrier.  Both groups pass the same 2n + 2 barriers after the prologue.
+  // runs its matrix work for tile j (partial S(j), then P(j-1)V(j-1)) while
+  // group B adds partials and runs softmax(j-1); in slot 2j+1 the other way
+  // round.  K(j) (stage j&1) is read in slots 2j and 2j+1, V(j) (stage j&1)
+  // in slots 2j+2 and 2j+3.  Group A issues K(j+1) at the start of slot 2j
+  // (into the stage K(j-1) left) and group B issues V(j) at the start of
+  // slot 2j (into the stage V(j-2) left); each waits for its loads before
+  // the barrier that ends slot 2j+1.  A wave's partial is written in its
+  // matrix slot and read by its partner in the next slot.  Both groups pass
+  // the same 2n + 1 barriers after the prologue's; group B's last P.V and
+  // group A's epilogue run after the last one.
   if (group == 0) {
-    scores(0);
-    __syncthreads();
-    softmax(kv_start);
-    if (n_tiles > 1) {
-      lstore(1);
-      if (n_tiles > 2) gload(kv_start + 2 * kGBN);
+    if (!FOLD || n_a > 0) {
+      scores(0);
+      publish();
     }
     __syncthreads();
-    for (int j = 1; j < n_tiles; ++j) {
-      const int kv0 = kv_start + j * kGBN;
-      pv((j - 1) & 1);
-      scores(j & 1);
+    if (!FOLD || n_a > 0) softmax(kv_start);
+    __syncthreads();
+    const int n_full = FOLD ? max(n_a, 1) : n_tiles;
+    for (int j = 1; j < n_full; ++j) {
+      if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
+      matrix(j & 1, (j - 1) & 1);
+      publish();
+      end_matrix_slot();
+      softmax(kv_start + j * kGBN);
+      landed();
       __syncthreads();
-      softmax(kv0);
-      if (j + 1 < n_tiles) {
-        lstore((j + 1) & 1);
-        if (j + 2 < n_tiles) gload(kv0 + 2 * kGBN);
+    }
+    if (FOLD) {
+      // Folded: A's last P.V in tile n_a's matrix slot, then K moves only.
+      int j = n_full;
+      if (n_a > 0 && n_a < n_tiles) {
+        if (n_a + 1 < n_tiles) move(kv_start + (n_a + 1) * kGBN, (n_a + 1) & 1);
+        pv((n_a - 1) & 1);
+        __syncthreads();
+        landed();
+        __syncthreads();
+        j = n_a + 1;
       }
-      __syncthreads();
+      for (; j < n_tiles; ++j) {
+        if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
+        __syncthreads();
+        landed();
+        __syncthreads();
+      }
     }
-    pv((n_tiles - 1) & 1);
-    __syncthreads();
+    if (!FOLD || n_a == n_tiles) pv((n_tiles - 1) & 1);
     __syncthreads();
   } else {
     __syncthreads();
-    // V(0) was loaded before the first barrier
     scores(0);
-    lstore(0);
-    if (n_tiles > 1) gload(kv_start + kGBN);
+    publish();
     __syncthreads();
     softmax(kv_start);
-    __syncthreads();
+    if (n_tiles > 1) move(kv_start + kGBN, 1);
+    end_soft_slot();
     for (int j = 1; j < n_tiles; ++j) {
-      const int kv0 = kv_start + j * kGBN;
-      pv((j - 1) & 1);
-      scores(j & 1);
-      lstore(j & 1);
-      if (j + 1 < n_tiles) gload(kv0 + kGBN);
+      matrix(j & 1, (j - 1) & 1);
+      publish();
+      landed();
       __syncthreads();
-      softmax(kv0);
-      __syncthreads();
+      softmax(kv_start + j * kGBN);
+      if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
+      end_soft_slot();
     }
     pv((n_tiles - 1) & 1);
-    __syncthreads();
   }
 
-  // ---- epilogue: O_w / l -> bf16, 4 consecutive columns per lane and block
+  // ---- epilogue: O_h / l -> bf16, 4 consecutive columns per lane and block
   const float l_tot = pair_sum(l_run);
   if (myq < w.len) {
     // a row without any visible key (malformed offsets only) is written as zeros
@@ -324,17 +456,26 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   }
 }
 
+template <class QT, class KVT, bool PAGED>
+void launch_d512_grid(const PrefillParams& p, uint64_t blocks, hipStream_t stream) {
+  if (p.fold && p.window == 0)
+    hipLaunchKernelGGL((prefill_d512_kernel<QT, KVT, PAGED, true>), dim3((uint32_t)blocks),
+                       dim3(kGThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((prefill_d512_kernel<QT, KVT, PAGED, false>), dim3((uint32_t)blocks),
+                       dim3(kGThreads), 0, stream, p);
+}
+
 template <class QT, class KVT>
 hipError_t launch_d512_one(PrefillParams p, hipStream_t stream) {
+  // (folded: ceil(ceil(n / 64) / 2) = ceil(n / 128) pairs for n tokens)
   const int64_t slots = (p.n_tokens + kGBM - 1) / kGBM + p.n_seqs;
   p.tile_slots = (int32_t)slots;
   const uint64_t blocks = dispatch_grid((uint64_t)slots * (uint64_t)p.n_q_heads);
   if (p.page_size > 0)
-    hipLaunchKernelGGL((prefill_d512_kernel<QT, KVT, true>), dim3((uint32_t)blocks),
-                       dim3(kGThreads), 0, stream, p);
+    launch_d512_grid<QT, KVT, true>(p, blocks, stream);
   else
-    hipLaunchKernelGGL((prefill_d512_kernel<QT, KVT, false>), dim3((uint32_t)blocks),
-                       dim3(kGThreads), 0, stream, p);
+    launch_d512_grid<QT, KVT, false>(p, blocks, stream);
   return hipGetLastError();
 }
 

@@ -57,11 +57,12 @@
  *
  * Grid shape.  For causal calls without a window whose grid would have at
  * most one workgroup per compute unit, each workgroup pairs a sequence's
- * 32-row query block r with block nb - 1 - r (nb blocks), so that every
- * workgroup sees about the same number of keys; the output is bitwise the
- * same as with the plain grid.  ATTN_PREFILL_FOLD=0 or =1 in the
- * environment turns this off, or on wherever the head grouping allows it
- * (for tests of both grids).
+ * query block r with block nb - 1 - r (nb blocks; 32 rows of four query
+ * heads for head_dim 64 and 128, 64 rows of one head for head_dim 512), so
+ * that every workgroup sees about the same number of keys; the output is
+ * bitwise the same as with the plain grid.  ATTN_PREFILL_FOLD=0 or =1 in
+ * the environment turns this off, or on wherever the head size and
+ * grouping allow it (for tests of both grids).
  */
 #ifndef ATTN_PREFILL_H
 #define ATTN_PREFILL_H

@@ -341,18 +341,22 @@ def test_folded_grid_matches_oracle_and_unfolded_bitwise(lengths, hq, hkv, monke
     assert torch.equal(folded, plain)
 
 
-@pytest.mark.parametrize("variant", ["chunked", "paged", "d64", "fp32q_fp16kv", "scale_neg"])
+@pytest.mark.parametrize("variant", ["chunked", "paged", "d64", "fp32q_fp16kv", "scale_neg",
+                                     "d512", "d512_chunked", "d512_paged"])
 def test_folded_grid_variants(variant, monkeypatch):
     """Folding with a KV history, a paged cache, 64-d heads, fp32 Q with fp16
-    K/V, and a negative scale."""
+    K/V, a negative scale, and 512-d heads (64-row blocks of one head)."""
     hq, hkv, d, scale = 8, 2, 128, None
     kw = {}
     lengths = [190, 33, 400, 1]
-    if variant in ("chunked", "paged"):
+    if variant in ("chunked", "paged", "d512_chunked", "d512_paged"):
         kw["history"] = [500, 0, 129, 64]
     if variant == "d64":
         d = 64
         kw["head_dim"] = 64
+    if variant.startswith("d512"):
+        d = 512
+        kw["head_dim"] = 512
     if variant == "fp32q_fp16kv":
         kw.update(q_dtype="fp32", kv_dtype="fp16")
     if variant == "scale_neg":
@@ -360,10 +364,10 @@ def test_folded_grid_variants(variant, monkeypatch):
     w = workloads.custom(f"fold_{variant}", lengths, hq, hkv, seed=65, scale=scale, **kw)
     _announce(w.name)
     inp = workloads.make_inputs(w)
-    if variant == "paged":
+    if variant.endswith("paged"):
         k_pool, v_pool, table = to_paged(inp, 128, seed=9)
         folded, plain = _fold_pair(monkeypatch, lambda: run_paged(
-            inp, k_pool, v_pool, table, 128, hq, hkv, w.attn_scale, 0))
+            inp, k_pool, v_pool, table, 128, hq, hkv, w.attn_scale, 0, d=d))
         want = oracle.attention_paged(inp["q"], k_pool, v_pool, inp["cu_seqlens"], table,
                                       inp["kv_lengths"], 128, hq, hkv, w.attn_scale, 0)
     else:
