@@ -221,29 +221,59 @@ __global__ __launch_bounds__(kXThreads, 1) void prefill_wide_kernel(PrefillParam
     return (kv0 + kXBN - 1 <= hist + wq0) &&
            (p.window == 0 || kv0 >= hist + wq_last - p.window + 1);
   };
+  // The two products, every LDS operand read kAhead MFMAs ahead with the
+  // order pinned: with one wave per SIMD nothing else hides the read
+  // latency from the matrix core.
+  constexpr int kAhead = 4;
   auto scores = [&](int st) {
     const uint16_t* ks = kstage0 + st * C::K_ELEMS;
+    constexpr int N = C::DCH * kXKB;
+    auto operand = [&](int i) -> opv8 {
+      const int c = i / kXKB, kb = i % kXKB;
+      return *reinterpret_cast<const opv8*>(ks + (32 * kb + col) * C::KSTR + 16 * c + 8 * half);
+    };
+    opv8 buf[kAhead];
 #pragma unroll
-    for (int kb = 0; kb < kXKB; ++kb) s[kb] = (f32x16_t){};
+    for (int i = 0; i < kAhead; ++i) buf[i] = operand(i);
 #pragma unroll
-    for (int c = 0; c < C::DCH; ++c)
+    for (int i = 0; i < N; ++i) {
+      const opv8 a = buf[i % kAhead];
+      if (i + kAhead < N) buf[i % kAhead] = operand(i + kAhead);
+      const int c = i / kXKB, kb = i % kXKB;
+      s[kb] = OP::mfma(a, qf[c], c == 0 ? (f32x16_t){} : s[kb]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-      for (int kb = 0; kb < kXKB; ++kb) {
-        const opv8 a = *reinterpret_cast<const opv8*>(
-            ks + (32 * kb + col) * C::KSTR + 16 * c + 8 * half);
-        s[kb] = OP::mfma(a, qf[c], s[kb]);
-      }
+    for (int i = 0; i < N - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
   auto pv = [&](int st) {
     const uint16_t* vs = vstage0 + st * C::V_ELEMS;
+    constexpr int N = kXKT * C::DBLK;
+    auto operand = [&](int i) -> opv8 {
+      const int kt = i / C::DBLK, c = i % C::DBLK;
+      return *reinterpret_cast<const opv8*>(vs + (32 * c + col) * C::VSTR + 16 * kt + 8 * half);
+    };
+    opv8 buf[kAhead];
 #pragma unroll
-    for (int kt = 0; kt < kXKT; ++kt)
+    for (int i = 0; i < kAhead; ++i) buf[i] = operand(i);
 #pragma unroll
-      for (int c = 0; c < C::DBLK; ++c) {
-        const opv8 a = *reinterpret_cast<const opv8*>(
-            vs + (32 * c + col) * C::VSTR + 16 * kt + 8 * half);
-        o[c] = OP::mfma(a, pf[kt], o[c]);
-      }
+    for (int i = 0; i < N; ++i) {
+      const opv8 a = buf[i % kAhead];
+      if (i + kAhead < N) buf[i % kAhead] = operand(i + kAhead);
+      const int kt = i / C::DBLK, c = i % C::DBLK;
+      o[c] = OP::mfma(a, pf[kt], o[c]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < N - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
   };
   auto softmax = [&](int kv0) {
     if (!tile_full(kv0)) {
