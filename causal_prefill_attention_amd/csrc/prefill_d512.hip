@@ -323,9 +323,15 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   // End of a matrix slot: the partial written, then the barrier, without
   // waiting for this wave's K/V loads to LDS still in flight (they are waited
   // for at the end of the next slot, before the stage is read).
-  auto end_matrix_slot = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto end_matrix_slot = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+  };
   // End of a softmax slot that leaves K/V loads in flight (group B's).
-  auto end_soft_slot = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto end_soft_slot = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+  };
 
   // own partial plus the partner's (both read back: the scores leave the
   // registers after the matrix slot), masks, online softmax
@@ -389,8 +395,8 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
     __syncthreads();
     const int n_full = FOLD ? max(n_a, 1) : n_tiles;
     for (int j = 1; j < n_full; ++j) {
-      if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
       matrix(j & 1, (j - 1) & 1);
+      if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
       publish();
       end_matrix_slot();
       softmax(kv_start + j * kGBN);
