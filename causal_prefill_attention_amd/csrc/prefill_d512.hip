@@ -31,9 +31,11 @@
 //     one 1 KiB row per instruction, 16-byte chunk c of row r at position
 //     c ^ (r & 15) for K, c ^ 2 (r & 7) for V, so that the K operand reads
 //     (16 rows, 16 bytes each) and the transposing Vᵀ reads (4 rows, 32
-//     bytes each, per 16 lanes) meet no bank twice): group A moves K, group B moves V, each load issued two
-//     slots before the tile is read and waited for before the barrier that
-//     publishes it, with no staging registers.  Vᵀ operands come from the
+//     bytes each, per 16 lanes) meet no bank twice), with no staging
+//     registers: group A issues them after the operand reads of its matrix
+//     slot and waits for them at the end of its softmax slot, so that no
+//     wave has a load to LDS in flight while it reads operands (hipcc
+//     waits for such a load before any LDS read it cannot prove disjoint).  Vᵀ operands come from the
 //     transposing LDS read ds_read_b64_tr_b16.  LDS: two K and two V
 //     stages (128 KiB) and the partial scores of the eight waves (32 KiB).
 //   * Folded grids (causal, no window, about one workgroup per CU): group A
@@ -127,14 +129,15 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
   const int mypos = hist + myq;
   const int d0 = kGHalf * hf;  // first column of this wave's half
 
-  // ---- K (group A) or V (group B) tiles straight into LDS: wave i of the
-  // group moves rows 8i .. 8i + 7, one row per load, lane l the chunk that
-  // goes to position l of the row
-  const kvelem* src = group == 0
-      ? static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts + (int64_t)kvh * p.k_hs
-      : static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts + (int64_t)kvh * p.v_hs;
-  const int64_t src_ts = group == 0 ? p.k_ts : p.v_ts;
-  const int row_bytes = (int)(src_ts * (int64_t)sizeof(kvelem));
+  // ---- K and V tiles straight into LDS (group A's waves): wave i moves
+  // rows 8i .. 8i + 7, one row per load, lane l the chunk that goes to
+  // position l of the row
+  const kvelem* const kseq =
+      static_cast<const kvelem*>(p.k) + (int64_t)w.kstart * p.k_ts + (int64_t)kvh * p.k_hs;
+  const kvelem* const vseq =
+      static_cast<const kvelem*>(p.v) + (int64_t)w.kstart * p.v_ts + (int64_t)kvh * p.v_hs;
+  const int k_row_bytes = (int)(p.k_ts * (int64_t)sizeof(kvelem));
+  const int v_row_bytes = (int)(p.v_ts * (int64_t)sizeof(kvelem));
   auto tile_slot = [&](int kv0) -> int64_t {
     if (!PAGED) return kv0;
     const int* row = p.block_table + (int64_t)w.seq * p.table_stride;
@@ -142,19 +145,30 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
     const int page = min(max(row[idx], 0), p.n_pages - 1);
     return (int64_t)page * p.page_size + (kv0 - idx * p.page_size);
   };
-  auto move = [&](int kv0, int st) {
-    // rows past the last visible key read as zero (buffer range)
+  // buffer resource of the K or V tile at kv0: rows past the last visible
+  // key read as zero (buffer range)
+  auto tile_rsrc = [&](int kv0, bool vtile) {
+    const kvelem* const src = vtile ? vseq : kseq;
+    const int64_t src_ts = vtile ? p.v_ts : p.k_ts;
+    const int row_bytes = vtile ? v_row_bytes : k_row_bytes;
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kv_hi - kv0, kGBN)));
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<kvelem*>(src + tile_slot(kv0) * src_ts), 0, rows * row_bytes, kRsrcWord3);
-    uint16_t* stage = kvs + (2 * group + st) * kGTile;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<kvelem*>(src + tile_slot(kv0) * src_ts),
+                                             0, rows * row_bytes, kRsrcWord3);
+  };
+  auto move = [&](__amdgpu_buffer_rsrc_t r, int st, bool vtile) {
+    const int row_bytes = vtile ? v_row_bytes : k_row_bytes;
+    uint16_t* stage = kvs + (2 * (vtile ? 1 : 0) + st) * kGTile;
+    // (offsets formed here from an opaque copy of the lane index rather than
+    // kept live across the tile loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < kGBN / 4; ++i) {
       const int row = (kGBN / 4) * (wave & 3) + i;
-      const int key = group == 0 ? (row & 15) : 2 * (row & 7);
+      const int key = vtile ? 2 * (row & 7) : (row & 15);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void*)(stage + row * kGD), 16,
-          row * row_bytes + 16 * (lane ^ key), 0, 0, 0);
+          row * row_bytes + 16 * (ln ^ key), 0, 0, 0);
     }
   };
   // the loads this wave issued have reached LDS (before the barrier that
@@ -327,11 +341,6 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
     __builtin_amdgcn_s_barrier();
   };
-  // End of a softmax slot that leaves K/V loads in flight (group B's).
-  auto end_soft_slot = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
-    __builtin_amdgcn_s_barrier();
-  };
 
   // own partial plus the partner's (both read back: the scores leave the
   // registers after the matrix slot), masks, online softmax
@@ -368,35 +377,45 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
 
   // ---- prologue: K(0) and K(1) (group A) or V(0) (group B) in LDS, Q in
   // registers
-  move(kv_start, 0);
-  if (group == 0 && n_tiles > 1) move(kv_start + kGBN, 1);
+  if (group == 0) move(tile_rsrc(kv_start, false), 0, false);
   load_q_op<DCH, OP>(qrow, half, qmul, qf);
   landed();
   __syncthreads();
 
   // ---- ping-pong slots (the 128-d kernel's schedule).  In slot 2j group A
-  // runs its matrix work for tile j (partial S(j), then P(j-1)V(j-1)) while
+  // runs its matrix work for tile j (P(j-1)V(j-1), then partial S(j)) while
   // group B adds partials and runs softmax(j-1); in slot 2j+1 the other way
   // round.  K(j) (stage j&1) is read in slots 2j and 2j+1, V(j) (stage j&1)
-  // in slots 2j+2 and 2j+3.  Group A issues K(j+1) at the start of slot 2j
-  // (into the stage K(j-1) left) and group B issues V(j) at the start of
-  // slot 2j (into the stage V(j-2) left); each waits for its loads before
-  // the barrier that ends slot 2j+1.  A wave's partial is written in its
-  // matrix slot and read by its partner in the next slot.  Both groups pass
-  // the same 2n + 1 barriers after the prologue's; group B's last P.V and
-  // group A's epilogue run after the last one.
+  // in slots 2j+2 and 2j+3.  Group A alone moves the tiles: after the last
+  // operand read of its matrix slot 2j it issues K(j+1) (into the stage
+  // K(j-1) left) and V(j) (into the stage V(j-2) left), and waits for them
+  // before the barrier that ends its softmax slot 2j+1; no wave has a load
+  // to LDS in flight while it reads operands.  A wave's partial is written
+  // in its matrix slot and read by its partner in the next slot.  Both
+  // groups pass the same 2n + 1 barriers after the prologue's; group B's
+  // last P.V and group A's epilogue run after the last one.
   if (group == 0) {
-    if (!FOLD || n_a > 0) {
-      scores(0);
-      publish();
-    }
-    __syncthreads();
+    // K(j + 1) and V(j) after the reads of matrix slot 2j
+    // (both descriptors first: any spilled value they need is reloaded, and
+    // waited for, before the first load to LDS is in flight)
+    auto move_after = [&](int j) {
+      const bool k_next = j + 1 < n_tiles;
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kv_start + (k_next ? j + 1 : j) * kGBN, false);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(kv_start + j * kGBN, true);
+      if (k_next) move(rk, (j + 1) & 1, false);
+      move(rv, j & 1, true);
+    };
+    if (!FOLD || n_a > 0) scores(0);
+    move_after(0);
+    if (!FOLD || n_a > 0) publish();
+    end_matrix_slot();
     if (!FOLD || n_a > 0) softmax(kv_start);
+    landed();
     __syncthreads();
     const int n_full = FOLD ? max(n_a, 1) : n_tiles;
     for (int j = 1; j < n_full; ++j) {
       matrix(j & 1, (j - 1) & 1);
-      if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
+      move_after(j);
       publish();
       end_matrix_slot();
       softmax(kv_start + j * kGBN);
@@ -404,19 +423,19 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
       __syncthreads();
     }
     if (FOLD) {
-      // Folded: A's last P.V in tile n_a's matrix slot, then K moves only.
+      // Folded: A's last P.V in tile n_a's matrix slot, then moves only.
       int j = n_full;
       if (n_a > 0 && n_a < n_tiles) {
-        if (n_a + 1 < n_tiles) move(kv_start + (n_a + 1) * kGBN, (n_a + 1) & 1);
         pv((n_a - 1) & 1);
-        __syncthreads();
+        move_after(n_a);
+        end_matrix_slot();
         landed();
         __syncthreads();
         j = n_a + 1;
       }
       for (; j < n_tiles; ++j) {
-        if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
-        __syncthreads();
+        move_after(j);
+        end_matrix_slot();
         landed();
         __syncthreads();
       }
@@ -427,18 +446,15 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_d512_kernel(PrefillParam
     __syncthreads();
     scores(0);
     publish();
-    __syncthreads();
+    end_matrix_slot();
     softmax(kv_start);
-    if (n_tiles > 1) move(kv_start + kGBN, 1);
-    end_soft_slot();
+    __syncthreads();
     for (int j = 1; j < n_tiles; ++j) {
       matrix(j & 1, (j - 1) & 1);
       publish();
-      landed();
-      __syncthreads();
+      end_matrix_slot();
       softmax(kv_start + j * kGBN);
-      if (j + 1 < n_tiles) move(kv_start + (j + 1) * kGBN, (j + 1) & 1);
-      end_soft_slot();
+      __syncthreads();
     }
     pv((n_tiles - 1) & 1);
   }
