@@ -68,6 +68,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             f"{path} is missing: build it with "
             "`python -m causal_prefill_attention_amd.build_lib` "
             "(there is no CPU fallback)")
+    # torch first: its bundled HIP runtime carries the soname the library
+    # asks for, so the library then shares torch's runtime (devices, streams,
+    # memory).  Loaded first, the library would pull in the system runtime
+    # and torch a second one, and the library's would see no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     lib.attn_prefill.restype = ctypes.c_int
     lib.attn_prefill.argtypes = [

@@ -35,6 +35,24 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_library_shares_one_hip_runtime_with_torch():
+    """Loading the library before anything imports torch still leaves one
+    HIP runtime in the process (two runtimes leave the library's without a
+    device)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from causal_prefill_attention_amd import binding\n"
+        "binding.load_library()\n"
+        "import torch\n"
+        "maps = open('/proc/self/maps').read().splitlines()\n"
+        "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         timeout=300, check=True).stdout
+    assert out.strip().splitlines()[-1] == "1"
+
+
 def test_status_strings_and_head_dims():
     lib = B.load_library()
     for code in (B.ATTN_OK, B.ATTN_ERR_INVALID_ARG, B.ATTN_ERR_UNSUPPORTED,
